@@ -1,0 +1,295 @@
+/*
+ * Paged GQA attention -- the CPU oracle (test infrastructure, never product).
+ *
+ * Plain, slow, obviously correct fp64 C.  Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg call this code; the HIP library never links
+ * or includes it, and it includes nothing from the HIP library.
+ *
+ * Inputs are bf16 bit patterns (uint16) widened exactly to double, as the RL.cu
+ * "Add Cuda Kernel" page's tests feed their CPU reference the already-rounded
+ * values (section "tests/test_attention.cu", prefill test setup).  `scale` is
+ * the fp32 value the GPU receives, widened.
+ *
+ * Every routine computes the definition directly: gather the sequence's keys
+ * and values through the block table, form all scores, take the exact maximum,
+ * exponentiate, normalize, weight the values.  No tiling, no online softmax,
+ * no reordering beyond what the definitions state.
+ *
+ * Pins (tests/test_oracle.py): brute-force attention over contiguous K/V on
+ * tiny inputs, closed forms (one token returns its value; equal keys or a zero
+ * query return the mean of V), block-shuffle and V-scaling invariance,
+ * split-equals-unsplit for the partial/merge pair, causal prefill against a
+ * textbook square-causal brute force, and one-row prefill against decode.
+ *
+ * ORACLE_MUTANT selects a planted mistake (0 = none).  The test suite builds
+ * each mutant into a scratch library and requires that some pin rejects it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+static double bf16_to_double(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_mutant(void) { return ORACLE_MUTANT; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* kv head serving query head h: consecutive query heads share one kv head
+ * (RL.cu page, attention.cuh comment "kv_head = q_head * H_kv / H_q"). */
+static int kv_head_of(int h, int Hq, int Hkv) {
+#if ORACLE_MUTANT == 2
+    return h % Hkv;
+#else
+    return (int)(((long)h * Hkv) / Hq);
+#endif
+}
+
+/* Address of token t's row of kv head g for sequence s: the logical block
+ * t / bs is looked up in the block table, the slot is t % bs (RL.cu page,
+ * paged decode kernel: "logical block index -> physical block in the pool";
+ * cache layout [num_blocks, H_kv, block_size, D]). */
+static const uint16_t *kv_row(const uint16_t *cache, const int32_t *block_tables,
+                              int s, int t, int g, int Hkv, int bs, int D, int mbps) {
+    long phys = block_tables[(long)s * mbps + t / bs];
+#if ORACLE_MUTANT == 4
+    int slot = (t + 1) % bs;
+#else
+    int slot = t % bs;
+#endif
+    return cache + (((phys * Hkv + g) * (long)bs + slot) * (long)D);
+}
+
+static const uint16_t *q_row(const uint16_t *q, long row, int h, int Hq, int D, long rows) {
+#if ORACLE_MUTANT == 14
+    (void)Hq;
+    return q + ((long)h * rows + row) * D;
+#else
+    (void)rows;
+    return q + (row * Hq + h) * (long)D;
+#endif
+}
+
+/* Scaled score z_t = scale * q . k_t (BI-V100 design page, section 1
+ * "Problem Definition": softmax(Q[h] K[t]^T / sqrt(d)) V[t]). */
+static double score(const uint16_t *qr, const uint16_t *kr, int D, double scale) {
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += bf16_to_double(qr[d]) * bf16_to_double(kr[d]);
+#if ORACLE_MUTANT == 1
+    (void)scale;
+    return acc;
+#else
+    return scale * acc;
+#endif
+}
+
+/* softmax over keys [t0, t1) of sequence s, weighted sum of values:
+ * m = max z, l = sum exp(z - m), out = sum exp(z - m) v / l.
+ * Returns m and l through the pointers (used by the partial routine). */
+static void attend_range(const uint16_t *qr, const uint16_t *k_cache, const uint16_t *v_cache,
+                         const int32_t *block_tables, int s, int g, int t0, int t1,
+                         int Hkv, int bs, int D, int mbps, double scale,
+                         double *z, double *out, double *m_out, double *l_out) {
+#if ORACLE_MUTANT == 3
+    t1 += 1; /* reads one slot past the end */
+#endif
+    int n = t1 - t0;
+    double m = -INFINITY;
+    for (int i = 0; i < n; ++i) {
+        const uint16_t *kr = kv_row(k_cache, block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
+        z[i] = score(qr, kr, D, scale);
+        if (z[i] > m) m = z[i];
+    }
+    double l = 0.0;
+    for (int i = 0; i < n; ++i) {
+#if ORACLE_MUTANT == 5
+        z[i] = exp(m - z[i]);
+#else
+        z[i] = exp(z[i] - m);
+#endif
+#if ORACLE_MUTANT == 7
+        if (i > 0) l += z[i]; /* drops the first term of the denominator */
+#else
+        l += z[i];
+#endif
+    }
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    for (int i = 0; i < n; ++i) {
+#if ORACLE_MUTANT == 6
+        const uint16_t *vr = kv_row(k_cache, block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
+#else
+        const uint16_t *vr = kv_row(v_cache, block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
+#endif
+        for (int d = 0; d < D; ++d) out[d] += z[i] * bf16_to_double(vr[d]);
+    }
+    for (int d = 0; d < D; ++d) out[d] /= l;
+    *m_out = m;
+    *l_out = l;
+}
+
+/* O1 -- decode output.  out[s, h, :] = softmax(scale * q[s,h] . K_s) V_s over
+ * the seq_lens[s] tokens of sequence s (seq_lens counts the current token,
+ * RL.cu page, attention.cuh comment on seq_lens).  A zero length writes zeros. */
+int oracle_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                  const int32_t *block_tables, const int32_t *seq_lens,
+                  int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
+    if (Hq % Hkv != 0) return 2;
+    long pairs = (long)S * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < pairs; ++i) {
+        int s = (int)(i / Hq), h = (int)(i % Hq);
+        int L = seq_lens[s];
+        double *o = out + i * D;
+        if (L <= 0) { for (int d = 0; d < D; ++d) o[d] = 0.0; continue; }
+        double *z = (double *)malloc(sizeof(double) * (size_t)(L + 1));
+        double m, l;
+        attend_range(q_row(q, s, h, Hq, D, S), k_cache, v_cache, block_tables, s,
+                     kv_head_of(h, Hq, Hkv), 0, L, Hkv, bs, D, mbps, (double)scale, z, o, &m, &l);
+        free(z);
+    }
+    return 0;
+}
+
+/* O2 -- decode partials.  Partition p of sequence s covers tokens
+ * [p*P, min((p+1)*P, L)); it yields the exact max of its scaled scores
+ * (max_logits), the sum of exp(z - max) (exp_sums) and the value average
+ * weighted by exp(z - max) / exp_sum (tmp_out).  The BI-V100 design page
+ * (section 2, "attention_partial") keeps the unnormalized weighted sum; the
+ * normalized form stored here differs from it by the factor exp_sum, which the
+ * merge multiplies back.  Partitions at or beyond ceil(L / P) are not written. */
+int oracle_decode_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                           const int32_t *block_tables, const int32_t *seq_lens,
+                           int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
+                           int P, int NP, double *max_logits, double *exp_sums, double *tmp_out) {
+    if (Hq % Hkv != 0 || P <= 0) return 2;
+    long work = (long)S * Hq * NP;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < work; ++i) {
+        int p = (int)(i % NP);
+        long sh = i / NP;
+        int s = (int)(sh / Hq), h = (int)(sh % Hq);
+        int L = seq_lens[s];
+        int nparts = (L + P - 1) / P;
+        if (p >= nparts) continue;
+        int t0 = p * P;
+#if ORACLE_MUTANT == 9
+        int t1 = (p + 1) * P + 1 < L ? (p + 1) * P + 1 : L;
+#else
+        int t1 = (p + 1) * P < L ? (p + 1) * P : L;
+#endif
+        double *z = (double *)malloc(sizeof(double) * (size_t)(t1 - t0 + 1));
+        double m, l;
+        double *o = tmp_out + i * D;
+        attend_range(q_row(q, s, h, Hq, D, S), k_cache, v_cache, block_tables, s,
+                     kv_head_of(h, Hq, Hkv), t0, t1, Hkv, bs, D, mbps, (double)scale, z, o, &m, &l);
+#if ORACLE_MUTANT == 8
+        for (int d = 0; d < D; ++d) o[d] *= l;
+#endif
+        max_logits[i] = m;
+        exp_sums[i] = l;
+        free(z);
+    }
+    return 0;
+}
+
+/* O3 -- cross-partition merge (BI-V100 design page, section 2 "combine" and
+ * "Level 3: Cross-Partition Coordination"): with M = max_p m_p and weights
+ * w_p = exp(m_p - M) * l_p, out = sum_p w_p * o_p / sum_p w_p over the
+ * ceil(L / P) partitions that exist. */
+int oracle_reduce(const double *max_logits, const double *exp_sums, const double *tmp_out,
+                  const int32_t *seq_lens, int S, int Hq, int D, int P, int NP, double *out) {
+    if (P <= 0) return 2;
+    long pairs = (long)S * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < pairs; ++i) {
+        int s = (int)(i / Hq);
+        int L = seq_lens[s];
+        int nparts = (L + P - 1) / P;
+        double *o = out + i * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (nparts <= 0) continue;
+        const double *ml = max_logits + i * NP;
+        const double *es = exp_sums + i * NP;
+        double M = -INFINITY;
+        for (int p = 0; p < nparts; ++p) if (ml[p] > M) M = ml[p];
+        double wsum = 0.0;
+        for (int p = 0; p < nparts; ++p) {
+#if ORACLE_MUTANT == 10
+            double w = exp(ml[p] - M);
+#else
+            double w = exp(ml[p] - M) * es[p];
+#endif
+            wsum += w;
+            const double *op = tmp_out + (i * NP + p) * (long)D;
+            for (int d = 0; d < D; ++d) o[d] += w * op[d];
+        }
+        for (int d = 0; d < D; ++d) o[d] /= wsum;
+    }
+    return 0;
+}
+
+/* O4 -- ragged paged prefill.  Sequence s owns query rows
+ * [cu[s], cu[s+1]) of the packed [total_q, H_q, D] tensor (AstrAI page,
+ * "Q Scheduling and KV Addressing": qo_indptr).  Its n = cu[s+1] - cu[s] new
+ * tokens are the last n of its seq_lens[s] cached-plus-new tokens, so row j
+ * sits at absolute position c + j with c = L - n, and it attends to keys
+ * t <= c + j (the causal rule of the RL.cu page's prefill kernel, aligned to
+ * the end of the context). */
+int oracle_prefill(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                   const int32_t *block_tables, const int32_t *seq_lens, const int32_t *cu_seqlens,
+                   int S, int total_q, int Hq, int Hkv, int D, int bs, int mbps, float scale,
+                   double *out) {
+    if (Hq % Hkv != 0) return 2;
+    long work = (long)total_q * Hq;
+    for (long i = 0; i < work * D; ++i) out[i] = 0.0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long w = 0; w < work; ++w) {
+        long row = w / Hq;
+        int h = (int)(w % Hq);
+        int s = 0;
+        while (s < S && !(cu_seqlens[s] <= row && row < cu_seqlens[s + 1])) ++s;
+        if (s >= S) continue;
+        int n = cu_seqlens[s + 1] - cu_seqlens[s];
+        int L = seq_lens[s];
+        int c = L - n;
+        if (c < 0) continue;
+        int j = (int)(row - cu_seqlens[s]);
+#if ORACLE_MUTANT == 11
+        int t1 = c + j;         /* drops the diagonal */
+#elif ORACLE_MUTANT == 12
+        int t1 = j + 1;         /* top-left alignment */
+#else
+        int t1 = c + j + 1;     /* keys t <= c + j */
+#endif
+        if (t1 <= 0) continue;
+        long qrow = row;
+#if ORACLE_MUTANT == 13
+        qrow = (row + 1) % total_q;
+#endif
+        double *z = (double *)malloc(sizeof(double) * (size_t)(t1 + 1));
+        double m, l;
+        attend_range(q_row(q, qrow, h, Hq, D, total_q), k_cache, v_cache, block_tables, s,
+                     kv_head_of(h, Hq, Hkv), 0, t1, Hkv, bs, D, mbps, (double)scale, z,
+                     out + w * D, &m, &l);
+        free(z);
+    }
+    return 0;
+}
