@@ -1,0 +1,139 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged GQA attention library.
+ *
+ * Three device entry points plus host helpers.  All pointers to tensors are
+ * DEVICE pointers owned by the caller; the library never allocates, frees or
+ * synchronizes.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL = the default stream).  Every entry point validates its scalar
+ * arguments on the host first and returns a status without launching
+ * anything on error; there is no fallback to another implementation.
+ * Device-resident values (block ids, seq_lens, cu_seqlens) are not checked:
+ * out-of-range values are undefined behaviour.
+ *
+ * Data types and layouts (row-major, contiguous):
+ *   q, out       bf16  [num_seqs, H_q, D]           decode
+ *                bf16  [total_q,  H_q, D]           prefill (packed ragged rows)
+ *   k_cache,
+ *   v_cache      bf16  [num_blocks, H_kv, block_size, D]
+ *   block_tables int32 [num_seqs, max_blocks_per_seq]   logical -> physical block
+ *   seq_lens     int32 [num_seqs]   KV length INCLUDING the current / new tokens
+ *   cu_seqlens   int32 [num_seqs + 1]  cu[0] = 0, non-decreasing (prefill rows)
+ *   max_logits,
+ *   exp_sums     fp32  [num_seqs, H_q, max_num_partitions]
+ *   tmp_out      fp32  [num_seqs, H_q, max_num_partitions, D]
+ * The cache layout and the block-table walk are those of the RL.cu
+ * "Add Cuda Kernel" page (include/kernels/attention.cuh, paged decode
+ * launcher); the partial names follow the BI-V100 paged-attention design page,
+ * section 2 "Level 3: Cross-Partition Coordination"; cu_seqlens is the
+ * qo_indptr of the AstrAI "CUDA Kernels" page, "Q Scheduling and KV
+ * Addressing".  Query head h reads kv head h / (H_q / H_kv).
+ *
+ * Supported: head_dim in {64, 128, 256}; block_size 16; H_q % H_kv == 0 with
+ * H_q / H_kv <= 16; partition_size a multiple of block_size.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum paged_attn_status {
+    PA_OK = 0,
+    PA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
+    PA_ERR_BAD_SHAPE = 2,     /* non-positive size, H_q % H_kv, partition size, buffer too small */
+    PA_ERR_UNSUPPORTED = 3,   /* head_dim, block_size or GQA group outside the supported set */
+    PA_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
+    PA_ERR_ALIGNMENT = 5      /* a bf16 / fp32 tensor pointer is not 16-byte aligned */
+};
+
+/*
+ * Paged GQA decode: for every sequence s and query head h,
+ *   out[s,h,:] = softmax(scale * q[s,h,:] . K_s^T) V_s
+ * over the seq_lens[s] tokens whose K/V rows are found through
+ * block_tables[s, t / block_size], slot t % block_size (BI-V100 design page,
+ * section 1 "Problem Definition"; RL.cu page, paged decode kernel).
+ *
+ * partition_size == 0: one pass per sequence; writes `out` (bf16, rounded to
+ *   nearest even).  max_logits / exp_sums / tmp_out are ignored (may be NULL).
+ * partition_size  > 0: split-KV.  Partition p of sequence s covers tokens
+ *   [p*P, min((p+1)*P, L)).  For p < ceil(L / P) it writes
+ *     max_logits[s,h,p] = exact max of the scaled scores (natural-log units),
+ *     exp_sums[s,h,p]   = sum of exp(score - max_logits),
+ *     tmp_out[s,h,p,:]  = sum exp(score - max_logits) v / exp_sums
+ *   (the BI-V100 page's "attention_partial", with the weighted value sum
+ *   stored normalized).  Partitions at or beyond ceil(L / P) are not written.
+ *   `out` is ignored; paged_attn_decode_reduce merges the partials.
+ *   max_num_partitions must be >= paged_attn_num_partitions(max_blocks_per_seq,
+ *   block_size, partition_size).
+ * A sequence with seq_lens[s] == 0 gets zeros (single pass) / no partials.
+ * num_seqs == 0 is a no-op returning PA_OK.
+ */
+int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                      int partition_size, void *out, float *max_logits, float *exp_sums,
+                      float *tmp_out, int max_num_partitions, void *stream);
+
+/*
+ * Cross-partition merge (BI-V100 design page, section 2 "combine" and
+ * "Level 3"): for each (s, h), with n = ceil(seq_lens[s] / partition_size),
+ *   M = max_{p<n} max_logits[s,h,p],  w_p = exp(max_logits[s,h,p] - M) * exp_sums[s,h,p],
+ *   out[s,h,:] = bf16( sum_p w_p tmp_out[s,h,p,:] / sum_p w_p ).
+ * A sequence with seq_lens[s] == 0 gets zeros.  Reads only p < n.
+ */
+int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
+                             const float *tmp_out, const int32_t *seq_lens, int num_seqs,
+                             int num_q_heads, int head_dim, int partition_size,
+                             int max_num_partitions, void *out, void *stream);
+
+/*
+ * Ragged paged prefill with a causal mask.  Sequence s owns query rows
+ * [cu_seqlens[s], cu_seqlens[s+1]) of q / out ([total_q, H_q, D]); its
+ * n = cu[s+1] - cu[s] new tokens are the LAST n of its seq_lens[s] tokens,
+ * whose K/V are already in the cache.  Row j (absolute position c + j,
+ * c = seq_lens[s] - n) attends to keys t <= c + j (AstrAI page, "Q Scheduling
+ * and KV Addressing"; causal rule of the RL.cu page's prefill kernel, aligned
+ * to the end of the context).  max_q_len must be >= every n (it sizes the
+ * launch); total_q must equal cu_seqlens[num_seqs].  Requires
+ * seq_lens[s] >= n for every s.
+ */
+int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens,
+                              const int32_t *cu_seqlens, int num_seqs, int total_q,
+                              int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq,
+                              float scale, void *out, void *stream);
+
+/* ---- host-only helpers (no device work) ---------------------------------- */
+
+/* Partition count covering max_blocks_per_seq * block_size tokens; 1 when
+ * partition_size == 0; -1 on a bad argument. */
+int paged_attn_num_partitions(int max_blocks_per_seq, int block_size, int partition_size);
+
+/* A partition size for paged_attn_decode: 0 (single pass) when one workgroup
+ * per (sequence, kv head) already fills the GPU several times over, otherwise
+ * a power of two >= 256 chosen so that the partition count is large enough to
+ * keep all compute units busy.  total_kv_tokens may be 0 (unknown). */
+int paged_attn_choose_partition_size(int num_seqs, int num_kv_heads, int max_seq_len,
+                                     long total_kv_tokens);
+
+/* Q-tile work map of a packed ragged batch (AstrAI page, "Q Scheduling and KV
+ * Addressing"): from HOST cu_seqlens, tile k covers rows
+ * [tile_to_index[k] * tile_rows, ...) of sequence tile_to_batch[k].  Writes at
+ * most `capacity` entries and returns the number of tiles (or -1 on a bad
+ * argument); a return value above capacity means the arrays were too small. */
+int paged_attn_prefill_tile_map(const int32_t *cu_seqlens_host, int num_seqs, int tile_rows,
+                                int32_t *tile_to_batch, int32_t *tile_to_index, int capacity);
+
+/* Human-readable name of a status code. */
+const char *paged_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,208 @@
+// C ABI of the paged attention library: host-side argument validation, the
+// partition-size heuristic, the prefill tile map, and dispatch to the kernels.
+// Validation happens entirely on the host before anything is enqueued; a
+// rejected call launches nothing and never falls back to other code.
+#include <limits.h>
+#include <stdint.h>
+
+#include "pa_launch.h"
+#include "paged_attn.h"
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxGroup = 16;
+constexpr int kGridYZMax = 65535;
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Checks shared by decode and prefill; returns PA_OK or a status.
+int check_common(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                 int max_blocks_per_seq) {
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL_POINTER;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0 || head_dim <= 0 || block_size <= 0)
+        return PA_ERR_BAD_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kGridYZMax || num_kv_heads > kGridYZMax) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGNMENT;
+    return PA_OK;
+}
+
+float log2e_scaled(float scale) { return (float)((double)scale * 1.4426950408889634074); }
+
+}  // namespace
+
+extern "C" {
+
+const char *paged_attn_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL_POINTER: return "null pointer";
+        case PA_ERR_BAD_SHAPE: return "bad shape";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_LAUNCH: return "kernel launch failed";
+        case PA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int paged_attn_num_partitions(int max_blocks_per_seq, int block_size, int partition_size) {
+    if (max_blocks_per_seq <= 0 || block_size <= 0 || partition_size < 0) return -1;
+    if (partition_size == 0) return 1;
+    const long long n = ceil_div((long long)max_blocks_per_seq * block_size, partition_size);
+    return n > INT_MAX ? -1 : (int)n;
+}
+
+int paged_attn_choose_partition_size(int num_seqs, int num_kv_heads, int max_seq_len,
+                                     long total_kv_tokens) {
+    // Aim for at least ~8 workgroups per compute unit of the 256-CU device
+    // while keeping partitions >= 256 tokens (so the partial record and the
+    // merge stay a few percent of the KV stream) and <= 2048 (balance).
+    constexpr long long kTargetWorkgroups = 8LL * 256;
+    if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 0;
+    const long long tokens = total_kv_tokens > 0 ? (long long)total_kv_tokens
+                                                 : (long long)num_seqs * max_seq_len;
+    int best = 256;
+    for (int p = 2048; p >= 256; p >>= 1) {
+        // Sum over sequences of ceil(L / P) is at least tokens / P and at most that plus num_seqs.
+        const long long wgs = (long long)num_kv_heads * (tokens / p + num_seqs / 2);
+        if (wgs >= kTargetWorkgroups) { best = p; break; }
+    }
+    if (best >= max_seq_len && (long long)num_seqs * num_kv_heads >= kTargetWorkgroups) return 0;
+    return best;
+}
+
+int paged_attn_prefill_tile_map(const int32_t *cu_seqlens_host, int num_seqs, int tile_rows,
+                                int32_t *tile_to_batch, int32_t *tile_to_index, int capacity) {
+    if (!cu_seqlens_host || num_seqs < 0 || tile_rows <= 0 || capacity < 0) return -1;
+    if (capacity > 0 && (!tile_to_batch || !tile_to_index)) return -1;
+    long long count = 0;
+    for (int b = 0; b < num_seqs; ++b) {
+        const long long n = (long long)cu_seqlens_host[b + 1] - cu_seqlens_host[b];
+        if (n < 0) return -1;
+        const long long tiles = ceil_div(n, tile_rows);
+        for (long long i = 0; i < tiles; ++i, ++count) {
+            if (count < capacity) {
+                tile_to_batch[count] = b;
+                tile_to_index[count] = (int32_t)i;
+            }
+        }
+    }
+    return count > INT_MAX ? -1 : (int)count;
+}
+
+int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, float scale, int partition_size,
+                      void *out, float *max_logits, float *exp_sums, float *tmp_out,
+                      int max_num_partitions, void *stream) {
+    int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
+    if (st != PA_OK) return st;
+    if (partition_size < 0 || partition_size % kBlockSize != 0) return PA_ERR_BAD_SHAPE;
+    int nparts = 1;
+    if (partition_size == 0) {
+        if (!out) return PA_ERR_NULL_POINTER;
+        if (!aligned16(out)) return PA_ERR_ALIGNMENT;
+    } else {
+        if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL_POINTER;
+        nparts = paged_attn_num_partitions(max_blocks_per_seq, block_size, partition_size);
+        if (nparts <= 0 || max_num_partitions < nparts) return PA_ERR_BAD_SHAPE;
+        if (!aligned16(tmp_out)) return PA_ERR_ALIGNMENT;
+    }
+    if (num_seqs == 0) return PA_OK;
+    pa::DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_cache = static_cast<const uint16_t *>(k_cache);
+    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale_log2 = log2e_scaled(scale);
+    a.partition_size = partition_size;
+    a.num_partitions = nparts;
+    a.max_num_partitions = partition_size ? max_num_partitions : 1;
+    a.out = static_cast<uint16_t *>(out);
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.tmp_out = tmp_out;
+    a.stream = static_cast<hipStream_t>(stream);
+    return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
+                             const float *tmp_out, const int32_t *seq_lens, int num_seqs,
+                             int num_q_heads, int head_dim, int partition_size,
+                             int max_num_partitions, void *out, void *stream) {
+    if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !out) return PA_ERR_NULL_POINTER;
+    if (num_seqs < 0 || num_q_heads <= 0 || partition_size <= 0 || max_num_partitions <= 0 ||
+        partition_size % kBlockSize != 0)
+        return PA_ERR_BAD_SHAPE;
+    if (!head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kGridYZMax) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(tmp_out) || !aligned16(out)) return PA_ERR_ALIGNMENT;
+    if (num_seqs == 0) return PA_OK;
+    pa::ReduceArgs a;
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.tmp_out = tmp_out;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.head_dim = head_dim;
+    a.partition_size = partition_size;
+    a.max_num_partitions = max_num_partitions;
+    a.out = static_cast<uint16_t *>(out);
+    a.stream = static_cast<hipStream_t>(stream);
+    return pa::launch_reduce(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens,
+                              const int32_t *cu_seqlens, int num_seqs, int total_q, int max_q_len,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, float scale, void *out,
+                              void *stream) {
+    int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
+    if (st != PA_OK) return st;
+    if (!cu_seqlens || !out) return PA_ERR_NULL_POINTER;
+    if (total_q < 0 || max_q_len < 0) return PA_ERR_BAD_SHAPE;
+    if (!aligned16(out)) return PA_ERR_ALIGNMENT;
+    if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+    if (max_q_len > total_q) return PA_ERR_BAD_SHAPE;
+    pa::PrefillArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_cache = static_cast<const uint16_t *>(k_cache);
+    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.cu_seqlens = cu_seqlens;
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale_log2 = log2e_scaled(scale);
+    a.out = static_cast<uint16_t *>(out);
+    a.stream = static_cast<hipStream_t>(stream);
+    return pa::launch_prefill(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

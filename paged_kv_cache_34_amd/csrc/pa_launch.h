@@ -1,0 +1,53 @@
+// Host-side launch descriptors shared by the C ABI (api.hip) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+    const uint16_t *q;
+    const uint16_t *k_cache;
+    const uint16_t *v_cache;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int max_blocks_per_seq;
+    float scale_log2;          // scale * log2(e)
+    int partition_size;        // 0 = single pass
+    int num_partitions;        // grid.x
+    int max_num_partitions;    // row stride of the partial buffers
+    uint16_t *out;
+    float *max_logits, *exp_sums, *tmp_out;
+    hipStream_t stream;
+};
+
+struct ReduceArgs {
+    const float *max_logits, *exp_sums, *tmp_out;
+    const int32_t *seq_lens;
+    int num_seqs, num_q_heads, head_dim, partition_size, max_num_partitions;
+    uint16_t *out;
+    hipStream_t stream;
+};
+
+struct PrefillArgs {
+    const uint16_t *q;
+    const uint16_t *k_cache;
+    const uint16_t *v_cache;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    const int32_t *cu_seqlens;
+    int num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim;
+    int max_blocks_per_seq;
+    float scale_log2;
+    uint16_t *out;
+    hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_reduce(const ReduceArgs &a);
+hipError_t launch_prefill(const PrefillArgs &a);
+
+}  // namespace pa

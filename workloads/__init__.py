@@ -23,14 +23,17 @@ them fails parity instead of passing silently.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import List, Optional, Sequence
 
 import numpy as np
 
 POISON = 64.0
-_CHUNK = 1 << 24  # normal draws are generated in chunks of this many values
+_CHUNK = 1 << 22  # values per independently seeded chunk of random draws
+_THREADS = min(16, os.cpu_count() or 1)
 
 
 # --------------------------------------------------------------------------
@@ -51,19 +54,48 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
-    n = int(np.prod(shape))
+def _chunk_seeds(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.integers(0, 2 ** 63 - 1, size=max(1, (n + _CHUNK - 1) // _CHUNK), dtype=np.int64)
+
+
+def _parallel_chunks(n: int, seeds: np.ndarray, fill) -> np.ndarray:
+    """Fill a uint16 array of n values chunk by chunk; chunk i uses child seed i.
+
+    The result depends only on the seeds, not on the thread count."""
     out = np.empty(n, dtype=np.uint16)
-    for lo in range(0, n, _CHUNK):
-        hi = min(n, lo + _CHUNK)
-        out[lo:hi] = f32_to_bf16_bits(rng.standard_normal(hi - lo, dtype=np.float32))
-    return out.reshape(shape)
+    bounds = [(i, lo, min(n, lo + _CHUNK)) for i, lo in enumerate(range(0, n, _CHUNK))]
+
+    def work(b):
+        i, lo, hi = b
+        fill(np.random.default_rng(int(seeds[i])), out[lo:hi])
+
+    if len(bounds) <= 1:
+        for b in bounds:
+            work(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=_THREADS) as ex:
+            list(ex.map(work, bounds))
+    return out
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) draws rounded to bf16 bit patterns."""
+    n = int(np.prod(shape))
+
+    def fill(g, dst):
+        dst[:] = f32_to_bf16_bits(g.standard_normal(dst.size, dtype=np.float32))
+
+    return _parallel_chunks(n, _chunk_seeds(rng, n), fill).reshape(shape)
 
 
 def _poison_bits(rng: np.random.Generator, n: int) -> np.ndarray:
-    signs = rng.integers(0, 2, size=n, dtype=np.int8)
-    vals = np.where(signs == 1, POISON, -POISON).astype(np.float32)
-    return f32_to_bf16_bits(vals)
+    """Finite poison: +-POISON with random signs, as bf16 bit patterns."""
+    pos, neg = f32_to_bf16_bits(np.array([POISON, -POISON], dtype=np.float32))
+
+    def fill(g, dst):
+        dst[:] = np.where(g.integers(0, 2, size=dst.size, dtype=np.uint8) == 1, pos, neg)
+
+    return _parallel_chunks(n, _chunk_seeds(rng, n), fill)
 
 
 # --------------------------------------------------------------------------
