@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA decode hot path on one MI355X.
+
+One step = one full decode pass over one batch: the partition kernel
+(block-table gather, GQA group Q load, QK^T, online softmax, PV, partial
+epilogue) followed by the cross-partition merge kernel, on the caller's stream.
+The host-side partition heuristic runs once per workload (it only needs the
+table shape, no device data).
+
+Default workload: Llama-3-8B-shaped decode -- 32 sequences, H_q=32, H_kv=8,
+D=128, block_size 16, context lengths uniform in [512, 4096], blocks shuffled
+across a pool 1.25x the need, bf16 N(0,1) data (seeded, synthetic).  R
+independent copies of the KV pool and its tables (same lengths) are rotated
+step by step so that the 256 MB Infinity Cache cannot serve repeated reads.
+
+Output: one JSON line (metric, value = KV tokens/s over the timed steps, ...)
+with a `roofline` object for the partition kernel (HIP events around each of
+its launches in the timed region) and a `cpu_baseline` object (the fp64 CPU
+oracle timed on this host's cores on a bounded sample of the same workload).
+
+`--workload` selects another of the synthetic workloads for reporting (the
+long-context split-KV, large ragged batch, or ragged prefill cases).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV tokens/sec and achieved HBM GB/s (% of peak), paged GQA decode, 1 MI355X"
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_34_amd", "csrc", "decode.hip")
+PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_34_amd", "csrc", "prefill.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel_tag: str, source: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    if there is none for this kernel and workload or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel_tag}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([\d.eE+]+)", text, re.M)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha(source):
+        return None
+    return float(m_b.group(1))
+
+
+def ensure_library():
+    import paged_kv_cache_34_amd as pa
+    if not os.path.exists(pa.LIBRARY):
+        from paged_kv_cache_34_amd import build
+        build.build()
+    pa.library()
+    return pa
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+def decode_copies(workload: str, copies: int):
+    """`copies` cases with identical lengths and shapes, independent pools and tables."""
+    import numpy as np
+    import workloads
+    base = workloads.NAMED[workload]()
+    out = [base]
+    for r in range(1, copies):
+        rng = np.random.default_rng(10_000 * r + base.seed)
+        layout = "fragmented" if workload == "large_ragged_decode" else "shuffled"
+        out.append(workloads.build_case(f"{workload}#copy{r}", base.seed, base.seq_lens,
+                                        base.num_q_heads, base.num_kv_heads, base.head_dim,
+                                        layout=layout, rng=rng,
+                                        partition_size=base.partition_size,
+                                        max_blocks_per_seq=base.max_blocks_per_seq))
+    return out
+
+
+def to_device(case):
+    import numpy as np
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    d = dict(q=bf(case.q), k=bf(case.k_cache), v=bf(case.v_cache),
+             bt=torch.from_numpy(case.block_tables).cuda(), sl=torch.from_numpy(case.seq_lens).cuda())
+    if case.cu_seqlens is not None:
+        d["cu"] = torch.from_numpy(case.cu_seqlens).cuda()
+    return d
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on host cores, bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(case, seconds: float, prefill: bool):
+    import oracle
+    orc = oracle.get()
+    if prefill:
+        t0 = time.perf_counter()
+        orc.prefill_case(case)
+        dt = time.perf_counter() - t0
+        import numpy as np
+        n = (case.cu_seqlens[1:] - case.cu_seqlens[:-1]).astype(np.float64)
+        c = case.seq_lens - n
+        flops = 4.0 * case.head_dim * case.num_q_heads * float(np.sum(n * c + n * (n + 1) / 2))
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+                "kind": "oracle",
+                "sample": f"one full pass of the {case.name} workload ({case.total_q} query rows), "
+                          f"{dt:.1f} s wall"}
+    P = case.partition_size
+    reps, t_total = 0, 0.0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        if P:
+            ml, es, to = orc.partials_case(case, P)
+            orc.reduce(ml, es, to, case.seq_lens, P)
+        else:
+            orc.decode_case(case)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    what = "partials + merge" if P else "single-pass decode"
+    return {"value": case.kv_tokens * reps / t_total, "unit": "KV tokens/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"the full {case.name} workload ({case.num_seqs} sequences, {case.kv_tokens} KV "
+                      f"tokens), oracle {what}, repeated {reps}x in {t_total:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# runs
+# ---------------------------------------------------------------------------
+def run_decode(args, pa):
+    import numpy as np
+    import torch
+    copies = args.copies or (3 if args.workload == "llama3_8b_decode" else 2)
+    t0 = time.perf_counter()
+    cases = decode_copies(args.workload, copies)
+    log(f"generated {copies} copies of {args.workload} in {time.perf_counter() - t0:.1f} s")
+    c0 = cases[0]
+    if args.partition_size is not None:
+        P = args.partition_size
+    elif c0.partition_size:
+        P = c0.partition_size
+    else:
+        P = pa.paged_attn_choose_partition_size(c0.num_seqs, c0.num_kv_heads, int(c0.seq_lens.max()),
+                                                c0.kv_tokens)
+    devs = [to_device(c) for c in cases]
+    npart = pa.paged_attn_num_partitions(c0.max_blocks_per_seq, c0.block_size, P) if P else 1
+    ws = pa.DecodeWorkspace(c0.num_seqs, c0.num_q_heads, c0.head_dim, npart, "cuda") if P else None
+    out = torch.empty_like(devs[0]["q"])
+    scale = float(c0.scale)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        d = devs[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        if P:
+            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
+                                 max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
+                                 max_num_partitions=npart, stream=stream)
+        else:
+            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, 0, out=out,
+                                 stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if P:
+            pa.paged_attn_decode_reduce(ws.max_logits, ws.exp_sums, ws.tmp_out, d["sl"], P, out,
+                                        stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region 1: whole steps, nothing else on the stream
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    # timed region 2: the same steps with events around each partition-kernel launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    kv_bytes = c0.kv_bytes
+    tokens = c0.kv_tokens
+    step_gbps = kv_bytes / (ms_step * 1e-3) / 1e9
+    kern_gbps = kv_bytes / (ms_kernel * 1e-3) / 1e9
+    traffic = counter_traffic("decode", DECODE_SOURCE, args.workload)
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": c0.num_seqs,
+            "num_q_heads": c0.num_q_heads,
+            "num_kv_heads": c0.num_kv_heads,
+            "head_dim": c0.head_dim,
+            "block_size": c0.block_size,
+            "kv_tokens": tokens,
+            "seq_len_min": int(c0.seq_lens.min()),
+            "seq_len_max": int(c0.seq_lens.max()),
+            "partition_size": P,
+            "kv_pool_copies_rotated": copies,
+        },
+        "hbm_gbps": step_gbps,
+        "hbm_pct_of_peak": 100.0 * step_gbps / PEAK_HBM_GBPS,
+        "accumulate": "fp32",
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel",
+            "achieved": kern_gbps,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": kern_gbps / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "kernel_ms": ms_kernel,
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    return result, cases[0]
+
+
+def run_prefill(args, pa):
+    import numpy as np
+    import torch
+    import workloads
+    case = workloads.ragged_prefill()
+    d = to_device(case)
+    out = torch.empty_like(d["q"])
+    stream = torch.cuda.current_stream()
+    scale = float(case.scale)
+
+    def step():
+        pa.paged_attn_prefill_ragged(d["q"], d["k"], d["v"], d["bt"], d["sl"], d["cu"], case.max_q_len,
+                                     scale, out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    n = (case.cu_seqlens[1:] - case.cu_seqlens[:-1]).astype(np.float64)
+    c = case.seq_lens - n
+    flops = 4.0 * case.head_dim * case.num_q_heads * float(np.sum(n * c + n * (n + 1) / 2))
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "causal TFLOP/s, ragged paged prefill, 1 MI355X",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ragged_prefill", "num_seqs": case.num_seqs, "total_q": case.total_q,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "kv_tokens": case.kv_tokens},
+        "kv_gbps": case.kv_bytes / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel", "achieved": tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": counter_traffic("prefill", PREFILL_SOURCE, "ragged_prefill"),
+                     "kernel_ms": ms, "algorithmic_flops_per_launch": flops},
+    }
+    return result, case
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_decode",
+                    choices=["llama3_8b_decode", "long_split_decode", "large_ragged_decode",
+                             "ragged_prefill", "tiny_decode"])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=None,
+                    help="independent KV pool copies rotated across steps (default 3, or 2 for >1 GB pools)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the decode would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pa = ensure_library()
+    if args.workload == "ragged_prefill":
+        result, case = run_prefill(args, pa)
+    else:
+        result, case = run_decode(args, pa)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, args.workload == "ragged_prefill")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

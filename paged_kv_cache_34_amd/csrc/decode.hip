@@ -35,39 +35,88 @@ namespace pa {
 
 constexpr int kBlock = 16;        // tokens per physical KV block
 constexpr float kLazyTau = 8.0f;  // log2 headroom of the lazy running max
+// Fourth word of a raw buffer descriptor on the GFX9 family (32-bit data, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D, int G, int NW>
 struct DecodeShape {
-    static constexpr int GP = (G + 3) / 4 * 4;   // head slots per token in LDS
-    static constexpr int NJ = D / 32;            // MFMA k-steps = 16-byte loads per lane per tile
+    static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+    static_assert(G >= 1 && G <= 16, "GQA group");
+    static constexpr int NJ = D / 32;            // K chunk loads per lane = S^T k-steps
+    static constexpr int NDT = D / 16;           // 16-dim tiles of O^T
     static constexpr int LPT = D / 8;            // lanes per token row in the V layout
     static constexpr int TPI = 64 / LPT;         // tokens per V load instruction
-    static constexpr int P_FLOATS = NW * (kBlock * GP + GP);
+    static constexpr int VROW = D + 16;          // bf16 per staged V row (32-byte pad)
+    static constexpr int STAGE_FLOATS = NW * kBlock * VROW / 2;
     static constexpr int RED_FLOATS = NW * G * D;
-    static constexpr int MAIN_FLOATS = RED_FLOATS > P_FLOATS ? RED_FLOATS : P_FLOATS;
-    static constexpr int STAT_FLOATS = 3 * NW * GP;
+    static constexpr int MAIN_FLOATS = RED_FLOATS > STAGE_FLOATS ? RED_FLOATS : STAGE_FLOATS;
+    static constexpr int STAT_FLOATS = 3 * NW * 16;
 };
 
-template <int D, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ seq_lens, int num_q_heads, int num_kv_heads,
-    int max_blocks_per_seq, float scale_log2, int partition_size, int max_num_partitions,
-    uint16_t *__restrict__ out, float *__restrict__ max_logits, float *__restrict__ exp_sums,
-    float *__restrict__ tmp_out) {
-    using S = DecodeShape<D, G, NW>;
-    constexpr int GP = S::GP, NJ = S::NJ, LPT = S::LPT, TPI = S::TPI;
-    __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+// Kernel argument block (validated on the host).
+struct DecodeParams {
+    const uint16_t *q, *k_cache, *v_cache;
+    const int32_t *block_tables, *seq_lens;
+    int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
+    float scale_log2;
+    int partition_size, max_num_partitions;
+    uint16_t *out;
+    float *max_logits, *exp_sums, *tmp_out;
+};
 
-    const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// One work item: partition `part` of kv head `kvh` of sequence `seq` (the whole
+// sequence when partition_size == 0), processed by the NW waves of the
+// calling workgroup; `lds` is the workgroup's scratch (DecodeShape floats).
+//
+// Per 16-token tile a wave computes, with the MFMA lane layouts
+// (col = lane % 16, grp = lane / 16):
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = K tile straight from HBM,
+//                  lane: token col, 16-byte chunk 4j + grp; B = the query rows)
+//                 -> lane holds scores of head col for tokens 4 grp + i;
+//   online softmax per head (block max over the 4 lane groups with permlane
+//   swaps, lazy running max);
+//   O^T += V^T P^T (v_mfma_f32_16x16x16_bf16; A = V^T read from the staged
+//                  row-major V tile with ds_read_b64_tr_b16, B = the lane's own
+//                  probabilities, split into bf16 high and low parts so the
+//                  product keeps ~16 mantissa bits) -> lane holds dims
+//                  16 dt + 4 grp + i of head col.
+// The probabilities never leave the lane that computed them, and V is never
+// converted on the VALU.
+template <int D, int G, int NW, int DEPTH>
+__device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, int kvh, int part,
+                                            float *lds) {
+    using S = DecodeShape<D, G, NW>;
+    constexpr int NJ = S::NJ, NDT = S::NDT, LPT = S::LPT, TPI = S::TPI, VROW = S::VROW;
+    const uint16_t *__restrict__ q = prm.q;
+    const int num_q_heads = prm.num_q_heads;
+    const int partition_size = prm.partition_size, max_num_partitions = prm.max_num_partitions;
+    const float scale_log2 = prm.scale_log2;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int h0 = kvh * G;
-    const int L = seq_lens[seq];
+    const int L = prm.seq_lens[seq];
     const int t_begin = partition_size ? part * partition_size : 0;
     if (t_begin >= L) {
         if (partition_size == 0) {  // empty sequence, single pass: zeros
-            uint16_t *o = out + ((long)seq * num_q_heads + h0) * D;
+            uint16_t *o = prm.out + ((long)seq * num_q_heads + h0) * D;
             for (int e = tid; e < G * D; e += NW * 64) o[e] = 0;
         }
         return;
@@ -77,177 +126,140 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     const int nb = (t_end + kBlock - 1) / kBlock - b_begin;
     const int my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
 
-    // S layout / MFMA operand lanes: r = token (B) or head row (A), cg = k group.
-    const int r = lane & 15, cg = lane >> 4;
-    // V layout lanes.
+    const int col = lane & 15, grp = lane >> 4;
     const int vcol = lane % LPT, vrow = lane / LPT;
 
-    u32x4 qa[NJ];
+    // query rows as the B operand of S^T: lane holds q[head col][chunk 4j + grp]
+    u32x4 qb[NJ];
     {
-        const uint16_t *qrow = q + ((long)seq * num_q_heads + h0 + (r < G ? r : 0)) * D;
+        const uint16_t *qrow = q + ((long)seq * num_q_heads + h0 + (col < G ? col : 0)) * D;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            u32x4 v = load_u32x4(qrow + (4 * j + cg) * 8);
-            qa[j] = (r < G) ? v : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 v = load_u32x4(qrow + (4 * j + grp) * 8);
+            qb[j] = (col < G) ? v : u32x4{0u, 0u, 0u, 0u};
         }
     }
 
     const long tile = (long)kBlock * D;
-    const long blk_stride = (long)num_kv_heads * tile;
-    const uint16_t *kbase = k_cache + kvh * tile + r * D + cg * 8;
-    const uint16_t *vbase = v_cache + kvh * tile + vrow * D + vcol * 8;
-    const int32_t *bt_row = block_tables + (long)seq * max_blocks_per_seq + b_begin + wave;
+    const long blk_stride = (long)prm.num_kv_heads * tile;
+    const uint16_t *kv_k = prm.k_cache + kvh * tile;
+    const uint16_t *kv_v = prm.v_cache + kvh * tile;
+    const int k_voff = (col * D + grp * 8) * 2;     // bytes within a tile
+    const int v_voff = (vrow * D + vcol * 8) * 2;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + b_begin + wave;
 
-    int ids = (lane < my_nb) ? bt_row[NW * lane] : 0;
+    // per-wave V staging tile [16][VROW] bf16
+    uint16_t *vstage = reinterpret_cast<uint16_t *>(lds) + wave * kBlock * VROW;
+    uint16_t *vst_wr = vstage + vrow * VROW + vcol * 8;
+    const uint16_t *vst_rd = vstage + (4 * grp + (col >> 2)) * VROW + 4 * (col & 3);
 
-    float m_run[4], m_ex[4], l_run[4];
+    f32x4 oT[NDT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m_run[i] = -INFINITY;
-        m_ex[i] = -INFINITY;
-        l_run[i] = 0.f;
-    }
-    float acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int dt = 0; dt < NDT; ++dt) oT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, m_ex = -INFINITY, l_run = 0.f;
 
-    float *p_lds = lds + wave * (kBlock * GP + GP);
-    float *a_lds = p_lds + kBlock * GP;
-
-    auto load_tile = [&](int i, u32x4 (&kr)[NJ], u32x4 (&vr)[NJ]) {
-        if ((i & 63) == 0 && i > 0) ids = (lane + i < my_nb) ? bt_row[NW * (lane + i)] : 0;
-        const long phys = __builtin_amdgcn_readlane(ids, i & 63);
-        const uint16_t *kp = kbase + phys * blk_stride;
-        const uint16_t *vp = vbase + phys * blk_stride;
+    // Loads tile slot `i` of the current 64-tile chunk with buffer loads whose
+    // descriptor covers exactly that tile; slots past the chunk get an empty
+    // descriptor, so their loads return zeros without touching memory and the
+    // loads stay unconditional (the compiler's wait counts stay exact).
+    auto load_tile = [&](int ids, int i, int n, u32x4 (&kr)[NJ], u32x4 (&vr)[NJ]) {
+        const bool ok = i < n;
+        const long phys = __builtin_amdgcn_readlane(ids, ok ? i : 0);
+        const int bytes = ok ? (int)(tile * 2) : 0;
+        const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)(kv_k + phys * blk_stride), 0, bytes, kBufferFlags);
+        const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(kv_v + phys * blk_stride), 0, bytes, kBufferFlags);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            kr[j] = load_u32x4(kp + j * 32);
-            vr[j] = load_u32x4(vp + j * TPI * D);
+            kr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + j * 64, 0, 0));
+            vr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + j * TPI * D * 2, 0, 0));
         }
     };
 
     auto compute_tile = [&](int i, const u32x4 (&kr)[NJ], const u32x4 (&vr)[NJ]) {
         const int tb = (b_begin + wave + NW * i) * kBlock;  // logical index of slot 0
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[j]),
-                                                         __builtin_bit_cast(bf16x8, kr[j]), sc, 0, 0, 0);
-        const bool tok_ok = tb + r < t_end;
-        float z[4], bm[4];
-        bool need = false;
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            z[i2] = tok_ok ? sc[i2] * scale_log2 : -INFINITY;
-            bm[i2] = row16_max(z[i2]);
-            need |= bm[i2] > m_run[i2] + kLazyTau;
-        }
-        const bool rescale = __any(need);
-        if (rescale) {
-            float al[4];
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const float mn = fmaxf(m_run[i2], bm[i2]);
-                al[i2] = fast_exp2(m_run[i2] - mn);
-                m_run[i2] = mn;
-                l_run[i2] *= al[i2];
-            }
-            if (r == 0 && 4 * cg < GP)
-                *reinterpret_cast<f32x4 *>(a_lds + 4 * cg) = f32x4{al[0], al[1], al[2], al[3]};
-        }
-        float p[4];
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            m_ex[i2] = fmaxf(m_ex[i2], bm[i2]);
-            p[i2] = fast_exp2(z[i2] - m_run[i2]);
-            l_run[i2] += p[i2];
-        }
-        if (4 * cg < GP) *reinterpret_cast<f32x4 *>(p_lds + r * GP + 4 * cg) = f32x4{p[0], p[1], p[2], p[3]};
-        wave_lds_sync();
-        if (rescale) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float al = a_lds[h];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-            }
-        }
         const bool tail = tb + kBlock > t_end;
+        // stage V (token rows past the end are zeroed so stale slots never reach PV)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int t = vrow + j * TPI;
-            float pv[GP];
+            const u32x4 v = (tail && tb + vrow + j * TPI >= t_end) ? u32x4{0u, 0u, 0u, 0u} : vr[j];
+            *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW) = v;
+        }
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h4 = 0; h4 < GP; h4 += 4) {
-                const f32x4 w = *reinterpret_cast<const f32x4 *>(p_lds + t * GP + h4);
-                pv[h4] = w[0];
-                pv[h4 + 1] = w[1];
-                pv[h4 + 2] = w[2];
-                pv[h4 + 3] = w[3];
-            }
-            float v[8];
+        for (int j = 0; j < NJ; ++j)
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[j]),
+                                                         __builtin_bit_cast(bf16x8, qb[j]), st, 0, 0, 0);
+        float z[4];
+        float bm = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[2 * k] = bf16_lo(vr[j][k]);
-                v[2 * k + 1] = bf16_hi(vr[j][k]);
-            }
-            if (tail && tb + t >= t_end) {
+        for (int i2 = 0; i2 < 4; ++i2) {
+            z[i2] = (tb + 4 * grp + i2 < t_end) ? st[i2] * scale_log2 : -INFINITY;
+            bm = fmaxf(bm, z[i2]);
+        }
+        bm = max_xor32(max_xor16(bm));
+        if (__any(bm > m_run + kLazyTau)) {
+            const float mn = fmaxf(m_run, bm);
+            const float al = fast_exp2(m_run - mn);
+            m_run = mn;
+            l_run *= al;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = 0.f;
-            }
+            for (int dt = 0; dt < NDT; ++dt) oT[dt] *= al;
+        }
+        m_ex = fmaxf(m_ex, bm);
+        float p[4];
 #pragma unroll
-            for (int h = 0; h < G; ++h)
+        for (int i2 = 0; i2 < 4; ++i2) p[i2] = fast_exp2(z[i2] - m_run);
+        l_run += (p[0] + p[1]) + (p[2] + p[3]);
+        const uint32_t h01 = cvt_pk_bf16(p[0], p[1]), h23 = cvt_pk_bf16(p[2], p[3]);
+        const uint32_t l01 = cvt_pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+        const uint32_t l23 = cvt_pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+        const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+        const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+        wave_lds_sync();
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
+        for (int dt = 0; dt < NDT; ++dt) {
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)(vst_rd + dt * 16));
+            oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, oT[dt], 0, 0, 0);
+            oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, oT[dt], 0, 0, 0);
         }
         wave_lds_sync();
     };
 
-    {
-        u32x4 ka[NJ], va[NJ], kb[NJ], vb[NJ];
-        if (my_nb > 0) load_tile(0, ka, va);
-        for (int i = 0; i < my_nb; i += 2) {
-            if (i + 1 < my_nb) load_tile(i + 1, kb, vb);
-            compute_tile(i, ka, va);
-            if (i + 2 < my_nb) load_tile(i + 2, ka, va);
-            if (i + 1 < my_nb) compute_tile(i + 1, kb, vb);
+    // Tiles are processed in chunks of 64 whose block ids sit one per lane;
+    // within a chunk a ring of DEPTH + 1 register tiles keeps tile i + DEPTH
+    // in flight while tile i is consumed.
+    for (int c0 = 0; c0 < my_nb; c0 += 64) {
+        const int n = min(64, my_nb - c0);
+        const int ids = (lane < n) ? bt_row[NW * (c0 + lane)] : 0;
+        u32x4 kbuf[DEPTH + 1][NJ], vbuf[DEPTH + 1][NJ];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_tile(ids, d, n, kbuf[d], vbuf[d]);
+        for (int i = 0; i < n; i += DEPTH + 1) {
+#pragma unroll
+            for (int u = 0; u <= DEPTH; ++u) {
+                load_tile(ids, i + u + DEPTH, n, kbuf[(u + DEPTH) % (DEPTH + 1)],
+                          vbuf[(u + DEPTH) % (DEPTH + 1)]);
+                if (i + u < n) compute_tile(c0 + i + u, kbuf[u], vbuf[u]);
+            }
         }
     }
 
     // ---- per-wave totals -------------------------------------------------
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) l_run[i2] = row16_sum(l_run[i2]);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = acc[h][e];
-#pragma unroll
-            for (int mask = LPT; mask < 64; mask <<= 1) a += xor_lane(a, mask);
-            acc[h][e] = a;
-        }
-
-    __syncthreads();  // every wave is done with its p slot before the buffer is reused
+    l_run = sum_xor32(sum_xor16(l_run));
+    __syncthreads();  // every wave is done with its staging tile before the buffer is reused
     float *red = lds;                      // [NW][G][D]
-    float *st_m = lds + S::MAIN_FLOATS;    // [NW][GP] running max (log2 units)
-    float *st_x = st_m + NW * GP;          // [NW][GP] exact max (log2 units)
-    float *st_l = st_x + NW * GP;          // [NW][GP] exp-sum relative to running max
-    if (lane < LPT) {
+    float *st_m = lds + S::MAIN_FLOATS;    // [NW][16] running max (log2 units)
+    float *st_x = st_m + NW * 16;          // [NW][16] exact max (log2 units)
+    float *st_l = st_x + NW * 16;          // [NW][16] exp-sum relative to running max
+    if (col < G) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float *dst = red + (wave * G + h) * D + vcol * 8;
-            *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-        }
-    }
-    if (r == 0 && 4 * cg < GP) {
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            st_m[wave * GP + 4 * cg + i2] = m_run[i2];
-            st_x[wave * GP + 4 * cg + i2] = m_ex[i2];
-            st_l[wave * GP + 4 * cg + i2] = l_run[i2];
+        for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<f32x4 *>(red + (wave * G + col) * D + 16 * dt + 4 * grp) = oT[dt];
+        if (grp == 0) {
+            st_m[wave * 16 + col] = m_run;
+            st_x[wave * 16 + col] = m_ex;
+            st_l[wave * 16 + col] = l_run;
         }
     }
     __syncthreads();
@@ -258,33 +270,109 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
         const int h = e / D, d = e % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, st_m[w * GP + h]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, st_m[w * 16 + h]);
         float lsum = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float f = fast_exp2(st_m[w * GP + h] - M);
-            lsum = fmaf(f, st_l[w * GP + h], lsum);
+            const float f = fast_exp2(st_m[w * 16 + h] - M);
+            lsum = fmaf(f, st_l[w * 16 + h], lsum);
             o = fmaf(f, red[(w * G + h) * D + d], o);
         }
         o = o / lsum;
         if (partition_size == 0)
-            out[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
+            prm.out[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
         else
-            tmp_out[((row0 + h) * max_num_partitions + part) * D + d] = o;
+            prm.tmp_out[((row0 + h) * max_num_partitions + part) * D + d] = o;
     }
     if (partition_size != 0 && tid < G) {
         const int h = tid;
         float M = -INFINITY, X = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            M = fmaxf(M, st_m[w * GP + h]);
-            X = fmaxf(X, st_x[w * GP + h]);
+            M = fmaxf(M, st_m[w * 16 + h]);
+            X = fmaxf(X, st_x[w * 16 + h]);
         }
         float lsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) lsum = fmaf(fast_exp2(st_m[w * GP + h] - M), st_l[w * GP + h], lsum);
-        max_logits[(row0 + h) * max_num_partitions + part] = X * kLn2;
-        exp_sums[(row0 + h) * max_num_partitions + part] = lsum * fast_exp2(M - X);
+        for (int w = 0; w < NW; ++w) lsum = fmaf(fast_exp2(st_m[w * 16 + h] - M), st_l[w * 16 + h], lsum);
+        prm.max_logits[(row0 + h) * max_num_partitions + part] = X * kLn2;
+        prm.exp_sums[(row0 + h) * max_num_partitions + part] = lsum * fast_exp2(M - X);
+    }
+    __syncthreads();  // the next item of a persistent workgroup reuses `lds`
+}
+
+// One workgroup per (partition, kv head, sequence); workgroups whose partition
+// starts past the sequence end exit at once.
+template <int D, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams prm) {
+    using S = DecodeShape<D, G, NW>;
+    __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    decode_item<D, G, NW, DEPTH>(prm, blockIdx.z, blockIdx.y, blockIdx.x, lds);
+}
+
+// Compact persistent split-KV: every workgroup first builds, in LDS, the
+// prefix over sequences of their item counts H_kv * ceil(L / P) (items are
+// ordered sequence, kv head, partition), then takes items blockIdx.x,
+// blockIdx.x + gridDim.x, ...  Only partitions that exist are ever visited, so
+// no workgroup is spent on the empty tail of an upper-bound grid.
+constexpr int kCompactMaxSeqs = 1024;
+
+template <int D, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodeParams prm) {
+    using S = DecodeShape<D, G, NW>;
+    constexpr int T = NW * 64;
+    constexpr int PER = (kCompactMaxSeqs + T - 1) / T;
+    __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    __shared__ int pref[kCompactMaxSeqs + 1];
+    __shared__ int wtot[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nseq = prm.num_seqs, P = prm.partition_size, hkv = prm.num_kv_heads;
+
+    int cnt[PER];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid * PER + k;
+        int c = 0;
+        if (i < nseq) {
+            const int L = prm.seq_lens[i];
+            c = L > 0 ? hkv * ((L + P - 1) / P) : 0;
+        }
+        cnt[k] = c;
+        local += c;
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid * PER + k;
+        run += cnt[k];
+        if (i < nseq) pref[i + 1] = run;
+    }
+    if (tid == 0) pref[0] = 0;
+    __syncthreads();
+
+    const int total = pref[nseq];
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        int lo = 0, hi = nseq;  // largest s with pref[s] <= item
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pref[mid] <= item) lo = mid; else hi = mid;
+        }
+        const int seq = __builtin_amdgcn_readfirstlane(lo);
+        const int np = (pref[seq + 1] - pref[seq]) / hkv;
+        const int rr = item - pref[seq];
+        const int kvh = __builtin_amdgcn_readfirstlane(rr / np);
+        const int part = __builtin_amdgcn_readfirstlane(rr % np);
+        decode_item<D, G, NW, DEPTH>(prm, seq, kvh, part, lds);
     }
 }
 
@@ -358,17 +446,62 @@ __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kDecodeWaves = 4;
+// Waves per decode workgroup and register prefetch depth (tiles in flight per
+// wave while one is consumed; deeper costs D/4 VGPRs per tile).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;
+#ifdef PA_DECODE_DEPTH
+constexpr int decode_depth(int) { return PA_DECODE_DEPTH; }
+#else
+constexpr int decode_depth(int) { return 1; }
+#endif
 constexpr int kReduceWaves = 4;
+
+#ifndef PA_DECODE_PERSIST_PER_CU
+#define PA_DECODE_PERSIST_PER_CU 0   // 0 = as many workgroups per CU as fit
+#endif
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeArgs &a) {
-    dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+    constexpr int DEPTH = decode_depth(D);
+    DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
+                     a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2,
+                     a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
+                     a.tmp_out};
     dim3 block(kDecodeWaves * 64);
-    hipLaunchKernelGGL((paged_decode_kernel<D, G, kDecodeWaves>), grid, block, 0, a.stream,
-                       a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_q_heads,
-                       a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2, a.partition_size,
-                       a.max_num_partitions, a.out, a.max_logits, a.exp_sums, a.tmp_out);
+    if (a.partition_size > 0 && a.num_seqs <= kCompactMaxSeqs) {
+        static int per_cu = 0;  // resident workgroups per CU for this instantiation
+        if (per_cu == 0) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH>, block.x, 0) != hipSuccess || n <= 0)
+                n = 1;
+            per_cu = PA_DECODE_PERSIST_PER_CU > 0 ? PA_DECODE_PERSIST_PER_CU : n;
+        }
+        const long upper = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
+        const long cap = (long)cu_count() * per_cu;
+        dim3 grid((unsigned)(upper < cap ? upper : cap));
+        hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH>), grid, block, 0,
+                           a.stream, prm);
+    } else {
+        dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+        hipLaunchKernelGGL((paged_decode_grid_kernel<D, G, kDecodeWaves, DEPTH>), grid, block, 0,
+                           a.stream, prm);
+    }
     return hipGetLastError();
 }
 

@@ -212,3 +212,11 @@ def test_nan_in_unused_slots_does_not_leak(orc):
     announce("NaN in tail slots")
     assert_out_close(bf16_host_f64(run_single(dev)), ref, "nan tail single")
     assert_out_close(bf16_host_f64(run_partials(dev, 32)[3]), ref, "nan tail merged")
+
+
+def test_many_sequences_use_the_grid_path(orc):
+    """More sequences than the compact split-KV path keeps in LDS (1024)."""
+    rng = np.random.default_rng(308)
+    lens = rng.integers(1, 300, size=1100)
+    case = workloads.build_case("many_seqs", 308, lens, 8, 2, 64)
+    check_case(orc, case, partitions=(0, 64), what="1100 sequences")
