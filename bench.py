@@ -14,9 +14,10 @@ independent copies of the KV pool and its tables (same lengths) are rotated
 step by step so that the 256 MB Infinity Cache cannot serve repeated reads.
 
 Output: one JSON line (metric, value = KV tokens/s over the timed steps, ...)
-with a `roofline` object for the partition kernel (HIP events around each of
-its launches in the timed region) and a `cpu_baseline` object (the fp64 CPU
-oracle timed on this host's cores on a bounded sample of the same workload).
+with a `roofline` object for the partition kernel (its average duration from
+HIP events around the same number of back-to-back launches on the stream the
+kernels run on) and a `cpu_baseline` object (the fp64 CPU oracle timed on this
+host's cores on a bounded sample of the same workload).
 
 `--workload` selects another of the synthetic workloads for reporting (the
 long-context split-KV, large ragged batch, or ragged prefill cases).
@@ -170,10 +171,8 @@ def run_decode(args, pa):
     scale = float(c0.scale)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         d = devs[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
         if P:
             pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
                                  max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
@@ -181,8 +180,6 @@ def run_decode(args, pa):
         else:
             pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, 0, out=out,
                                  stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         if P:
             pa.paged_attn_decode_reduce(ws.max_logits, ws.exp_sums, ws.tmp_out, d["sl"], P, out,
                                         stream=stream)
@@ -198,13 +195,29 @@ def run_decode(args, pa):
     stop.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
-    # timed region 2: the same steps with events around each partition-kernel launch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
+    # timed region 2: the partition kernel alone, the same launches back to back
+    # (one event pair around all of them, as a profiler times kernel execution)
+    def decode_only(i):
+        d = devs[i % copies]
+        if P:
+            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
+                                 max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
+                                 max_num_partitions=npart, stream=stream)
+        else:
+            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, 0, out=out,
+                                 stream=stream)
+
     torch.cuda.synchronize()
-    ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for i in range(args.steps):
+        decode_only(i)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    ms_kernel = k0.elapsed_time(k1) / args.steps
+    # leave the output of a full step behind (the partials above are not merged)
+    step(0)
+    torch.cuda.synchronize()
 
     kv_bytes = c0.kv_bytes
     tokens = c0.kv_tokens
@@ -302,6 +315,18 @@ def run_prefill(args, pa):
     return result, case
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
+                                           "copies": reps}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +340,8 @@ def main():
                     help="independent KV pool copies rotated across steps (default 3, or 2 for >1 GB pools)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (the reference kernel for HBM counter scaling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -327,6 +354,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     pa = ensure_library()
     if args.workload == "ragged_prefill":
         result, case = run_prefill(args, pa)

@@ -64,20 +64,21 @@ int paged_attn_num_partitions(int max_blocks_per_seq, int block_size, int partit
 
 int paged_attn_choose_partition_size(int num_seqs, int num_kv_heads, int max_seq_len,
                                      long total_kv_tokens) {
-    // Aim for at least ~8 workgroups per compute unit of the 256-CU device
-    // while keeping partitions >= 256 tokens (so the partial record and the
-    // merge stay a few percent of the KV stream) and <= 2048 (balance).
-    constexpr long long kTargetWorkgroups = 8LL * 256;
+    // Work items are (sequence, kv head, partition) triples.  Measured on
+    // MI355X: 512-token partitions are best until there are more than ~4096
+    // items, then 1024 (up to ~8192 items), then 2048.  Shorter partitions
+    // pay the per-item start-up (query, block ids, first tiles) too often;
+    // longer ones leave compute units idle at the end.  When one partition
+    // already covers the longest sequence and there are enough (sequence,
+    // kv head) pairs, a single pass avoids the partials and the merge.
     if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 0;
     const long long tokens = total_kv_tokens > 0 ? (long long)total_kv_tokens
                                                  : (long long)num_seqs * max_seq_len;
-    int best = 256;
-    for (int p = 2048; p >= 256; p >>= 1) {
-        // Sum over sequences of ceil(L / P) is at least tokens / P and at most that plus num_seqs.
-        const long long wgs = (long long)num_kv_heads * (tokens / p + num_seqs / 2);
-        if (wgs >= kTargetWorkgroups) { best = p; break; }
-    }
-    if (best >= max_seq_len && (long long)num_seqs * num_kv_heads >= kTargetWorkgroups) return 0;
+    auto items = [&](long long p) { return (long long)num_kv_heads * (tokens / p + num_seqs / 2 + 1); };
+    int best = 2048;
+    if (items(512) <= 4096) best = 512;
+    else if (items(1024) <= 8192) best = 1024;
+    if (best >= max_seq_len && (long long)num_seqs * num_kv_heads >= 1024) return 0;
     return best;
 }
 
@@ -153,7 +154,7 @@ int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
         partition_size % kBlockSize != 0)
         return PA_ERR_BAD_SHAPE;
     if (!head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
-    if (num_seqs > kGridYZMax) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kGridYZMax || num_q_heads > kGridYZMax) return PA_ERR_UNSUPPORTED;
     if (!aligned16(tmp_out) || !aligned16(out)) return PA_ERR_ALIGNMENT;
     if (num_seqs == 0) return PA_OK;
     pa::ReduceArgs a;

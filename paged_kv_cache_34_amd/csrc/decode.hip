@@ -376,67 +376,84 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     }
 }
 
-// Cross-partition merge: one workgroup per (query head, sequence).  Slots of
-// D/4 lanes each take partitions round-robin with 16-byte loads; slot sums are
-// folded in LDS in a fixed order.
-template <int D, int NW>
+// Cross-partition merge (the BI-V100 page's combine rule): one workgroup per
+// (64-dim chunk, query head, sequence).  Its 16 slots of 16 lanes (4 dims per
+// lane) take partitions round-robin, 4 at a time, each slot keeping a running
+// max so that a single pass suffices; the slots are then folded in LDS in a
+// fixed order (deterministic).
+constexpr int kReduceChunk = 64;   // dims per workgroup
+constexpr int kReduceUnroll = 4;   // partitions in flight per slot
+
+template <int NW>
 __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
     const float *__restrict__ max_logits, const float *__restrict__ exp_sums,
     const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens, int num_q_heads,
-    int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
-    constexpr int LPP = D / 4;
-    constexpr int PPW = 64 / LPP;
-    constexpr int SLOTS = NW * PPW;
-    __shared__ __attribute__((aligned(16))) float red[SLOTS * D];
-    __shared__ float wred[SLOTS];
-    __shared__ float smax[NW];
+    int head_dim, int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
+    constexpr int LPP = kReduceChunk / 4;  // lanes per partition row
+    constexpr int SLOTS = NW * 64 / LPP;
+    __shared__ __attribute__((aligned(16))) float red[SLOTS * kReduceChunk];
+    __shared__ float sm[SLOTS], sw[SLOTS];
 
-    const int h = blockIdx.x, seq = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
+    const int tid = threadIdx.x;
     const int L = seq_lens[seq];
     const int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
     const long row = (long)seq * num_q_heads + h;
-    uint16_t *o = out + row * D;
+    uint16_t *o = out + row * head_dim + chunk * kReduceChunk;
     if (n == 0) {
-        for (int d = tid; d < D; d += NW * 64) o[d] = 0;
+        for (int d = tid; d < kReduceChunk; d += NW * 64) o[d] = 0;
         return;
     }
     const float *mlr = max_logits + row * max_num_partitions;
     const float *esr = exp_sums + row * max_num_partitions;
-
-    float M = -INFINITY;
-    for (int p = tid; p < n; p += NW * 64) M = fmaxf(M, mlr[p]);
-    M = row16_max(M);
-    M = fmaxf(M, xor_lane(M, 16));
-    M = fmaxf(M, xor_lane(M, 32));
-    if (lane == 0) smax[wave] = M;
-    __syncthreads();
-    M = smax[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, smax[w]);
-
     const int slot = tid / LPP, dl = tid % LPP;
+    const float *base = tmp_out + row * (long)max_num_partitions * head_dim + chunk * kReduceChunk + dl * 4;
+
+    float m = -INFINITY, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    const float *base = tmp_out + row * (long)max_num_partitions * D + dl * 4;
-    for (int p = slot; p < n; p += SLOTS) {
-        const float w = fast_exp2((mlr[p] - M) * kLog2e) * esr[p];
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(base + (long)p * D);
-        acc[0] = fmaf(w, v[0], acc[0]);
-        acc[1] = fmaf(w, v[1], acc[1]);
-        acc[2] = fmaf(w, v[2], acc[2]);
-        acc[3] = fmaf(w, v[3], acc[3]);
-        wsum += w;
+    for (int p0 = slot; p0 < n; p0 += SLOTS * kReduceUnroll) {
+        float mv[kReduceUnroll], ev[kReduceUnroll];
+        f32x4 v[kReduceUnroll];
+#pragma unroll
+        for (int u = 0; u < kReduceUnroll; ++u) {
+            const int p = p0 + u * SLOTS;
+            const bool ok = p < n;
+            mv[u] = ok ? mlr[p] : -INFINITY;
+            ev[u] = ok ? esr[p] : 0.f;
+            v[u] = ok ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kReduceUnroll; ++u) {
+            if (mv[u] > m) {  // rescale what was accumulated to the new max
+                const float f = fast_exp2((m - mv[u]) * kLog2e);
+                acc *= f;
+                wsum *= f;
+                m = mv[u];
+            }
+            const float w = ev[u] > 0.f ? fast_exp2((mv[u] - m) * kLog2e) * ev[u] : 0.f;
+            acc[0] = fmaf(w, v[u][0], acc[0]);
+            acc[1] = fmaf(w, v[u][1], acc[1]);
+            acc[2] = fmaf(w, v[u][2], acc[2]);
+            acc[3] = fmaf(w, v[u][3], acc[3]);
+            wsum += w;
+        }
     }
-    *reinterpret_cast<f32x4 *>(red + slot * D + dl * 4) = acc;
-    if (dl == 0) wred[slot] = wsum;
+    *reinterpret_cast<f32x4 *>(red + slot * kReduceChunk + dl * 4) = acc;
+    if (dl == 0) {
+        sm[slot] = m;
+        sw[slot] = wsum;
+    }
     __syncthreads();
-    for (int d = tid; d < D; d += NW * 64) {
+    for (int d = tid; d < kReduceChunk; d += NW * 64) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) M = fmaxf(M, sm[sl]);
         float a = 0.f, ws = 0.f;
 #pragma unroll
         for (int sl = 0; sl < SLOTS; ++sl) {
-            a += red[sl * D + d];
-            ws += wred[sl];
+            const float f = sw[sl] > 0.f ? fast_exp2((sm[sl] - M) * kLog2e) : 0.f;
+            a = fmaf(f, red[sl * kReduceChunk + d], a);
+            ws = fmaf(f, sw[sl], ws);
         }
         o[d] = (uint16_t)f32_to_bf16_bits(a / ws);
     }
@@ -528,15 +545,6 @@ hipError_t launch_decode_d(const DecodeArgs &a, int G) {
     }
 }
 
-template <int D>
-hipError_t launch_reduce_d(const ReduceArgs &a) {
-    dim3 grid(a.num_q_heads, a.num_seqs);
-    dim3 block(kReduceWaves * 64);
-    hipLaunchKernelGGL((paged_reduce_kernel<D, kReduceWaves>), grid, block, 0, a.stream,
-                       a.max_logits, a.exp_sums, a.tmp_out, a.seq_lens, a.num_q_heads,
-                       a.partition_size, a.max_num_partitions, a.out);
-    return hipGetLastError();
-}
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a) {
@@ -550,12 +558,12 @@ hipError_t launch_decode(const DecodeArgs &a) {
 }
 
 hipError_t launch_reduce(const ReduceArgs &a) {
-    switch (a.head_dim) {
-        case 64: return launch_reduce_d<64>(a);
-        case 128: return launch_reduce_d<128>(a);
-        case 256: return launch_reduce_d<256>(a);
-        default: return hipErrorInvalidValue;
-    }
+    dim3 grid(a.head_dim / kReduceChunk, a.num_q_heads, a.num_seqs);
+    dim3 block(kReduceWaves * 64);
+    hipLaunchKernelGGL((paged_reduce_kernel<kReduceWaves>), grid, block, 0, a.stream, a.max_logits,
+                       a.exp_sums, a.tmp_out, a.seq_lens, a.num_q_heads, a.head_dim,
+                       a.partition_size, a.max_num_partitions, a.out);
+    return hipGetLastError();
 }
 
 }  // namespace pa

@@ -65,8 +65,12 @@ def test_choose_partition_size(lib):
     # small batch, long context: split-KV with a power of two >= 256
     p = pa.paged_attn_choose_partition_size(4, 4, 100_000, 400_000)
     assert p >= 256 and p & (p - 1) == 0
-    # tiny problem: still a valid split (never below 256)
-    assert pa.paged_attn_choose_partition_size(2, 1, 100, 137) == 256
+    # tiny problem with few (sequence, kv head) pairs: still split, never below 512
+    assert pa.paged_attn_choose_partition_size(2, 1, 100, 137) == 512
+    # the Llama-3-8B-shaped batch and the long-context batch use 512; the large ragged one 1024
+    assert pa.paged_attn_choose_partition_size(32, 8, 4096, 72260) == 512
+    assert pa.paged_attn_choose_partition_size(4, 4, 100_000, 400_000) == 512
+    assert pa.paged_attn_choose_partition_size(256, 8, 32768, 449037) == 1024
     # enough (sequence, kv head) pairs with short contexts: single pass
     assert pa.paged_attn_choose_partition_size(4096, 8, 128, 4096 * 128) == 0
     assert pa.paged_attn_choose_partition_size(0, 8, 128) == 0
