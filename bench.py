@@ -166,13 +166,22 @@ def run_decode(args, pa):
                                                 c0.kv_tokens)
     devs = [to_device(c) for c in cases]
     npart = pa.paged_attn_num_partitions(c0.max_blocks_per_seq, c0.block_size, P) if P else 1
-    ws = pa.DecodeWorkspace(c0.num_seqs, c0.num_q_heads, c0.head_dim, npart, "cuda") if P else None
+    ws = pa.DecodeWorkspace(c0.num_seqs, c0.num_q_heads, c0.head_dim, npart, "cuda",
+                            num_kv_heads=c0.num_kv_heads) if P else None
+    # the merge is a separate kernel unless --merge fused asks for the
+    # last-workgroup merge inside the partition kernel
+    fused = bool(P) and args.merge == "fused"
     out = torch.empty_like(devs[0]["q"])
     scale = float(c0.scale)
     stream = torch.cuda.current_stream()
 
     def step(i):
         d = devs[i % copies]
+        if fused:
+            pa.paged_attn_decode_fused(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P, out,
+                                       ws.max_logits, ws.exp_sums, ws.tmp_out, ws.counters,
+                                       stream=stream)
+            return
         if P:
             pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
                                  max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
@@ -199,6 +208,9 @@ def run_decode(args, pa):
     # (one event pair around all of them, as a profiler times kernel execution)
     def decode_only(i):
         d = devs[i % copies]
+        if fused:
+            step(i)
+            return
         if P:
             pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
                                  max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
@@ -248,6 +260,7 @@ def run_decode(args, pa):
             "seq_len_min": int(c0.seq_lens.min()),
             "seq_len_max": int(c0.seq_lens.max()),
             "partition_size": P,
+            "merge": "fused into the partition kernel" if fused else ("separate kernel" if P else "none (single pass)"),
             "kv_pool_copies_rotated": copies,
         },
         "hbm_gbps": step_gbps,
@@ -255,7 +268,7 @@ def run_decode(args, pa):
         "accumulate": "fp32",
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel",
+            "kernel": "paged_decode_compact_kernel (fused merge)" if fused else "paged_decode_compact_kernel",
             "achieved": kern_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -338,6 +351,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--copies", type=int, default=None,
                     help="independent KV pool copies rotated across steps (default 3, or 2 for >1 GB pools)")
+    ap.add_argument("--merge", default="separate", choices=["fused", "separate"],
+                    help="cross-partition merge: a separate kernel (default; faster on MI355X at "
+                         "these shapes) or fused into the partition kernel")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -91,6 +91,32 @@ int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
                              int max_num_partitions, void *out, void *stream);
 
 /*
+ * Decode with the cross-partition merge fused into the partition kernel (the
+ * BI-V100 design page, section 2 "Level 3": "a separate reduction kernel (or
+ * the last partition block)" -- this is the second option).  Same inputs and
+ * partial buffers as paged_attn_decode with partition_size > 0, which here
+ * are workspace; writes the bf16 `out` for every sequence in one launch.
+ * Each workgroup that writes a partial record increments the arrival counter
+ * of its (sequence, kv head); the workgroup completing the set merges the
+ * ceil(L / P) records in partition order (deterministic) and resets the
+ * counter.  Sequences with a single partition write `out` directly.
+ *   counters  int32 [num_seqs * num_kv_heads], device memory, all zero on
+ *             entry (e.g. cleared once after allocation); every completed call
+ *             leaves them zero.  Calls that overlap in time must not share a
+ *             counters buffer.
+ * partition_size must be > 0 (a multiple of block_size).  Best when a
+ * sequence has at most a few dozen partitions: the merge of one
+ * (sequence, kv head) runs in a single workgroup.
+ */
+int paged_attn_decode_fused(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int num_blocks, int max_blocks_per_seq, float scale,
+                            int partition_size, void *out, float *max_logits, float *exp_sums,
+                            float *tmp_out, int max_num_partitions, int32_t *counters,
+                            void *stream);
+
+/*
  * Ragged paged prefill with a causal mask.  Sequence s owns query rows
  * [cu_seqlens[s], cu_seqlens[s+1]) of q / out ([total_q, H_q, D]); its
  * n = cu[s+1] - cu[s] new tokens are the LAST n of its seq_lens[s] tokens,

@@ -51,6 +51,7 @@ def library() -> ctypes.CDLL:
             raise RuntimeError(f"{LIBRARY} is not built; run `python -m paged_kv_cache_34_amd.build`")
         lib = ctypes.CDLL(LIBRARY)
         lib.paged_attn_decode.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp]
+        lib.paged_attn_decode_fused.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp, _vp]
         lib.paged_attn_decode_reduce.argtypes = [_vp] * 4 + [_i] * 5 + [_vp, _vp]
         lib.paged_attn_prefill_ragged.argtypes = [_vp] * 6 + [_i] * 9 + [ctypes.c_float, _vp, _vp]
         lib.paged_attn_num_partitions.argtypes = [_i, _i, _i]
@@ -58,7 +59,8 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_prefill_tile_map.argtypes = [_vp, _i, _i, _vp, _vp, _i]
         lib.paged_attn_status_string.argtypes = [_i]
         lib.paged_attn_status_string.restype = ctypes.c_char_p
-        for fn in ("paged_attn_decode", "paged_attn_decode_reduce", "paged_attn_prefill_ragged",
+        for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
+                   "paged_attn_prefill_ragged",
                    "paged_attn_num_partitions", "paged_attn_choose_partition_size",
                    "paged_attn_prefill_tile_map"):
             getattr(lib, fn).restype = _i
@@ -130,6 +132,31 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
     _check("paged_attn_decode", st)
 
 
+def paged_attn_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                            partition_size: int, out, max_logits, exp_sums, tmp_out, counters,
+                            stream=None) -> None:
+    """Split-KV decode with the merge fused in: writes `out`; partials are workspace;
+    `counters` int32 [num_seqs * num_kv_heads] must be zero and is left zero."""
+    import torch
+    _want(q, torch.bfloat16, "q")
+    _want(k_cache, torch.bfloat16, "k_cache")
+    _want(v_cache, torch.bfloat16, "v_cache")
+    _want(block_tables, torch.int32, "block_tables")
+    _want(seq_lens, torch.int32, "seq_lens")
+    _want(out, torch.bfloat16, "out")
+    _want(counters, torch.int32, "counters")
+    for name, t in (("max_logits", max_logits), ("exp_sums", exp_sums), ("tmp_out", tmp_out)):
+        _want(t, torch.float32, name)
+    num_seqs, hq, d = q.shape
+    num_blocks, hkv, bs, _ = k_cache.shape
+    st = library().paged_attn_decode_fused(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), num_seqs, hq,
+        hkv, d, bs, num_blocks, block_tables.shape[1], float(scale), int(partition_size),
+        _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), tmp_out.shape[2],
+        _ptr(counters), _stream(stream))
+    _check("paged_attn_decode_fused", st)
+
+
 def paged_attn_decode_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: int, out,
                              stream=None) -> None:
     """Merge fp32 partials [S, H_q, NP(, D)] into bf16 `out` [S, H_q, D]."""
@@ -197,11 +224,14 @@ def paged_attn_status_string(status: int) -> str:
 # convenience: a full decode step (partials workspace from torch, two launches)
 # ---------------------------------------------------------------------------
 class DecodeWorkspace:
-    """fp32 partial buffers sized for (num_seqs, H_q, max_num_partitions, D)."""
+    """fp32 partial buffers sized for (num_seqs, H_q, max_num_partitions, D), plus
+    the zeroed arrival counters of the fused merge ([num_seqs * num_kv_heads])."""
 
-    def __init__(self, num_seqs, num_q_heads, head_dim, max_num_partitions, device):
+    def __init__(self, num_seqs, num_q_heads, head_dim, max_num_partitions, device,
+                 num_kv_heads: int = 0):
         import torch
         self.max_num_partitions = int(max_num_partitions)
+        self.counters = torch.zeros(max(1, num_seqs * num_kv_heads), dtype=torch.int32, device=device)
         self.max_logits = torch.empty((num_seqs, num_q_heads, max_num_partitions),
                                       dtype=torch.float32, device=device)
         self.exp_sums = torch.empty_like(self.max_logits)
@@ -210,8 +240,10 @@ class DecodeWorkspace:
 
 
 def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, partition_size: int,
-                 out=None, workspace: Optional[DecodeWorkspace] = None, stream=None):
-    """Decode into `out`: one pass if partition_size == 0, else partials then merge."""
+                 out=None, workspace: Optional[DecodeWorkspace] = None, stream=None,
+                 fused: bool = False):
+    """Decode into `out`: one pass if partition_size == 0, else partials then the
+    merge (a separate launch, or fused into the partition kernel)."""
     import torch
     if out is None:
         out = torch.empty_like(q)
@@ -222,7 +254,13 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, part
     bs = k_cache.shape[2]
     npart = paged_attn_num_partitions(block_tables.shape[1], bs, partition_size)
     if workspace is None:
-        workspace = DecodeWorkspace(q.shape[0], q.shape[1], q.shape[2], npart, q.device)
+        workspace = DecodeWorkspace(q.shape[0], q.shape[1], q.shape[2], npart, q.device,
+                                    num_kv_heads=k_cache.shape[1])
+    if fused:
+        paged_attn_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                                out, workspace.max_logits, workspace.exp_sums, workspace.tmp_out,
+                                workspace.counters, stream=stream)
+        return out
     paged_attn_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
                       max_logits=workspace.max_logits, exp_sums=workspace.exp_sums,
                       tmp_out=workspace.tmp_out, max_num_partitions=workspace.max_num_partitions,

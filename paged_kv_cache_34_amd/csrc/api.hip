@@ -101,21 +101,23 @@ int paged_attn_prefill_tile_map(const int32_t *cu_seqlens_host, int num_seqs, in
     return count > INT_MAX ? -1 : (int)count;
 }
 
-int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
-                      const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
-                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                      int num_blocks, int max_blocks_per_seq, float scale, int partition_size,
-                      void *out, float *max_logits, float *exp_sums, float *tmp_out,
-                      int max_num_partitions, void *stream) {
+namespace {
+int decode_common(const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                  int max_blocks_per_seq, float scale, int partition_size, void *out,
+                  float *max_logits, float *exp_sums, float *tmp_out, int max_num_partitions,
+                  int32_t *counters, void *stream) {
     int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
     if (st != PA_OK) return st;
     if (partition_size < 0 || partition_size % kBlockSize != 0) return PA_ERR_BAD_SHAPE;
     int nparts = 1;
-    if (partition_size == 0) {
+    if (partition_size == 0 || counters) {
         if (!out) return PA_ERR_NULL_POINTER;
         if (!aligned16(out)) return PA_ERR_ALIGNMENT;
-    } else {
+    }
+    if (partition_size > 0) {
         if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL_POINTER;
         nparts = paged_attn_num_partitions(max_blocks_per_seq, block_size, partition_size);
         if (nparts <= 0 || max_num_partitions < nparts) return PA_ERR_BAD_SHAPE;
@@ -141,8 +143,37 @@ int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
     a.max_logits = max_logits;
     a.exp_sums = exp_sums;
     a.tmp_out = tmp_out;
+    a.counters = counters;
     a.stream = static_cast<hipStream_t>(stream);
     return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+}  // namespace
+
+int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, float scale, int partition_size,
+                      void *out, float *max_logits, float *exp_sums, float *tmp_out,
+                      int max_num_partitions, void *stream) {
+    return decode_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                         partition_size, out, max_logits, exp_sums, tmp_out, max_num_partitions,
+                         nullptr, stream);
+}
+
+int paged_attn_decode_fused(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int num_blocks, int max_blocks_per_seq, float scale,
+                            int partition_size, void *out, float *max_logits, float *exp_sums,
+                            float *tmp_out, int max_num_partitions, int32_t *counters,
+                            void *stream) {
+    if (!counters) return PA_ERR_NULL_POINTER;
+    if (partition_size <= 0) return PA_ERR_BAD_SHAPE;
+    return decode_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                         partition_size, out, max_logits, exp_sums, tmp_out, max_num_partitions,
+                         counters, stream);
 }
 
 int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,

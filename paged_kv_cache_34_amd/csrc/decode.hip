@@ -62,6 +62,7 @@ struct DecodeParams {
     int partition_size, max_num_partitions;
     uint16_t *out;
     float *max_logits, *exp_sums, *tmp_out;
+    int *counters;  // fused merge: one arrival counter per (sequence, kv head); null = no merge
 };
 
 __device__ __forceinline__ float max_xor32(float x) {
@@ -99,9 +100,38 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 //                  16 dt + 4 grp + i of head col.
 // The probabilities never leave the lane that computed them, and V is never
 // converted on the VALU.
+// Partial-record element stores: plain, or agent-scope (coherent across the
+// XCDs' L2 caches) when the fused merge of another workgroup will read them.
+__device__ __forceinline__ void store_partial(float *p, float v, bool coherent) {
+    if (coherent)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+__device__ __forceinline__ float load_partial(float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block ids of the first 64 tiles a wave of the workgroup will take in the
+// item (one per lane), so that a persistent workgroup can fetch them for its
+// next item while it still works on the current one.
+template <int NW>
+__device__ __forceinline__ int item_first_ids(const DecodeParams &prm, int seq, int part, int L,
+                                              int wave, int lane) {
+    const int P = prm.partition_size;
+    const int t_begin = P ? part * P : 0;
+    const int t_end = P ? min(L, t_begin + P) : L;
+    const int b_begin = t_begin / kBlock;
+    const int nb = (t_end + kBlock - 1) / kBlock - b_begin;
+    const int my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + b_begin + wave;
+    return (lane < min(64, my_nb)) ? bt_row[NW * lane] : 0;
+}
+
+// `L` is seq_lens[seq]; `ids0` the item's first block ids (item_first_ids).
 template <int D, int G, int NW, int DEPTH>
 __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, int kvh, int part,
-                                            float *lds) {
+                                            int L, int ids0, float *lds) {
     using S = DecodeShape<D, G, NW>;
     constexpr int NJ = S::NJ, NDT = S::NDT, LPT = S::LPT, TPI = S::TPI, VROW = S::VROW;
     const uint16_t *__restrict__ q = prm.q;
@@ -112,7 +142,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int h0 = kvh * G;
-    const int L = prm.seq_lens[seq];
     const int t_begin = partition_size ? part * partition_size : 0;
     if (t_begin >= L) {
         if (partition_size == 0) {  // empty sequence, single pass: zeros
@@ -231,7 +260,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
     // in flight while tile i is consumed.
     for (int c0 = 0; c0 < my_nb; c0 += 64) {
         const int n = min(64, my_nb - c0);
-        const int ids = (lane < n) ? bt_row[NW * (c0 + lane)] : 0;
+        const int ids = c0 == 0 ? ids0 : ((lane < n) ? bt_row[NW * (c0 + lane)] : 0);
         u32x4 kbuf[DEPTH + 1][NJ], vbuf[DEPTH + 1][NJ];
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) load_tile(ids, d, n, kbuf[d], vbuf[d]);
@@ -265,7 +294,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
     __syncthreads();
 
     // ---- merge the waves (fixed order) and write ---------------------------
+    // The item writes bf16 output directly when it is the whole sequence
+    // (single pass, or the fused mode with one partition); otherwise its
+    // partial record.
     const long row0 = (long)seq * num_q_heads + h0;
+    const int nparts = partition_size ? (L + partition_size - 1) / partition_size : 1;
+    const bool fused = prm.counters != nullptr;
+    const bool direct = partition_size == 0 || (fused && nparts == 1);
     for (int e = tid; e < G * D; e += NW * 64) {
         const int h = e / D, d = e % D;
         float M = -INFINITY;
@@ -279,12 +314,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
             o = fmaf(f, red[(w * G + h) * D + d], o);
         }
         o = o / lsum;
-        if (partition_size == 0)
+        if (direct)
             prm.out[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
         else
-            prm.tmp_out[((row0 + h) * max_num_partitions + part) * D + d] = o;
+            store_partial(prm.tmp_out + ((row0 + h) * max_num_partitions + part) * D + d, o, fused);
     }
-    if (partition_size != 0 && tid < G) {
+    if (!direct && tid < G) {
         const int h = tid;
         float M = -INFINITY, X = -INFINITY;
 #pragma unroll
@@ -295,8 +330,54 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
         float lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) lsum = fmaf(fast_exp2(st_m[w * 16 + h] - M), st_l[w * 16 + h], lsum);
-        prm.max_logits[(row0 + h) * max_num_partitions + part] = X * kLn2;
-        prm.exp_sums[(row0 + h) * max_num_partitions + part] = lsum * fast_exp2(M - X);
+        store_partial(prm.max_logits + (row0 + h) * max_num_partitions + part, X * kLn2, fused);
+        store_partial(prm.exp_sums + (row0 + h) * max_num_partitions + part, lsum * fast_exp2(M - X), fused);
+    }
+    if (!direct && fused) {
+        // Fused cross-partition merge (the BI-V100 page, section 2 "Level 3":
+        // "or the last partition block"): publish the partial device-wide,
+        // count arrivals of the (sequence, kv head) partitions, and let the
+        // workgroup that completes the set merge them in partition order.
+        // The partial records were written with agent-scope (cross-XCD
+        // coherent) stores; each wave waits for its stores to complete, the
+        // barrier collects the waves, and only then is the arrival counted.
+        // The workgroup completing the set reads the records back with
+        // agent-scope loads, so no cache-wide writeback or invalidate is needed.
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        __syncthreads();
+        int *flag = reinterpret_cast<int *>(st_m);
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(prm.counters + (long)seq * prm.num_kv_heads + kvh, 1,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            flag[0] = (old == nparts - 1);
+        }
+        __syncthreads();
+        if (flag[0]) {
+            for (int e = tid; e < G * D; e += NW * 64) {
+                const int h = e / D, d = e % D;
+                float *mlr = prm.max_logits + (row0 + h) * max_num_partitions;
+                float *esr = prm.exp_sums + (row0 + h) * max_num_partitions;
+                float *tor = prm.tmp_out + (row0 + h) * max_num_partitions * (long)D + d;
+                float m = -INFINITY, wsum = 0.f, acc = 0.f;
+                for (int p = 0; p < nparts; ++p) {
+                    const float mp = load_partial(mlr + p);
+                    if (mp > m) {
+                        const float f = fast_exp2((m - mp) * kLog2e);
+                        acc *= f;
+                        wsum *= f;
+                        m = mp;
+                    }
+                    const float w = fast_exp2((mp - m) * kLog2e) * load_partial(esr + p);
+                    acc = fmaf(w, load_partial(tor + (long)p * D), acc);
+                    wsum += w;
+                }
+                prm.out[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(acc / wsum);
+            }
+            if (tid == 0)
+                __hip_atomic_store(prm.counters + (long)seq * prm.num_kv_heads + kvh, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();  // the next item of a persistent workgroup reuses `lds`
 }
@@ -307,7 +388,11 @@ template <int D, int G, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams prm) {
     using S = DecodeShape<D, G, NW>;
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
-    decode_item<D, G, NW, DEPTH>(prm, blockIdx.z, blockIdx.y, blockIdx.x, lds);
+    const int seq = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
+    const int L = prm.seq_lens[seq];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ids0 = item_first_ids<NW>(prm, seq, part, L, wave, threadIdx.x & 63);
+    decode_item<D, G, NW, DEPTH>(prm, seq, kvh, part, L, ids0, lds);
 }
 
 // Compact persistent split-KV: every workgroup first builds, in LDS, the
@@ -324,8 +409,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     constexpr int PER = (kCompactMaxSeqs + T - 1) / T;
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
     __shared__ int pref[kCompactMaxSeqs + 1];
+    __shared__ int lens[kCompactMaxSeqs];
     __shared__ int wtot[NW];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nseq = prm.num_seqs, P = prm.partition_size, hkv = prm.num_kv_heads;
 
     int cnt[PER];
@@ -337,6 +424,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
         if (i < nseq) {
             const int L = prm.seq_lens[i];
             c = L > 0 ? hkv * ((L + P - 1) / P) : 0;
+            lens[i] = L;
         }
         cnt[k] = c;
         local += c;
@@ -361,18 +449,42 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     __syncthreads();
 
     const int total = pref[nseq];
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        int lo = 0, hi = nseq;  // largest s with pref[s] <= item
+    // item -> (sequence, kv head, partition): largest s with pref[s] <= item
+    auto locate = [&](int item, int &seq, int &kvh, int &part) {
+        int lo = 0, hi = nseq;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (pref[mid] <= item) lo = mid; else hi = mid;
         }
-        const int seq = __builtin_amdgcn_readfirstlane(lo);
+        seq = __builtin_amdgcn_readfirstlane(lo);
         const int np = (pref[seq + 1] - pref[seq]) / hkv;
         const int rr = item - pref[seq];
-        const int kvh = __builtin_amdgcn_readfirstlane(rr / np);
-        const int part = __builtin_amdgcn_readfirstlane(rr % np);
-        decode_item<D, G, NW, DEPTH>(prm, seq, kvh, part, lds);
+        kvh = __builtin_amdgcn_readfirstlane(rr / np);
+        part = __builtin_amdgcn_readfirstlane(rr % np);
+    };
+    int item = blockIdx.x;
+    if (item >= total) return;
+    int seq, kvh, part;
+    locate(item, seq, kvh, part);
+    int L = lens[seq];
+    int ids = item_first_ids<NW>(prm, seq, part, L, wave, lane);
+    for (;;) {
+        // the next item's block ids are fetched while this one streams
+        const int next = item + gridDim.x;
+        int nseq_, nkvh, npart, nL = 0, nids = 0;
+        if (next < total) {
+            locate(next, nseq_, nkvh, npart);
+            nL = lens[nseq_];
+            nids = item_first_ids<NW>(prm, nseq_, npart, nL, wave, lane);
+        }
+        decode_item<D, G, NW, DEPTH>(prm, seq, kvh, part, L, ids, lds);
+        if (next >= total) break;
+        item = next;
+        seq = nseq_;
+        kvh = nkvh;
+        part = npart;
+        L = nL;
+        ids = nids;
     }
 }
 
@@ -396,46 +508,61 @@ __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
 
     const int chunk = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
     const int tid = threadIdx.x;
+    const long row = (long)seq * num_q_heads + h;
+    const float *mlr = max_logits + row * max_num_partitions;
+    const float *esr = exp_sums + row * max_num_partitions;
+    const int slot = tid / LPP, dl = tid % LPP;
+    const float *base = tmp_out + row * (long)max_num_partitions * head_dim + chunk * kReduceChunk + dl * 4;
+    // The first round of partition records is loaded before the sequence
+    // length is known (records past the sequence's partitions are discarded
+    // by selection, never used in arithmetic), which takes one dependent
+    // memory round trip off the kernel.
+    float mv[kReduceUnroll], ev[kReduceUnroll];
+    f32x4 v[kReduceUnroll];
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+        const int p = slot + u * SLOTS;
+        const bool in = p < max_num_partitions;
+        mv[u] = in ? mlr[p] : -INFINITY;
+        ev[u] = in ? esr[p] : 0.f;
+        v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const int L = seq_lens[seq];
     const int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
-    const long row = (long)seq * num_q_heads + h;
     uint16_t *o = out + row * head_dim + chunk * kReduceChunk;
     if (n == 0) {
         for (int d = tid; d < kReduceChunk; d += NW * 64) o[d] = 0;
         return;
     }
-    const float *mlr = max_logits + row * max_num_partitions;
-    const float *esr = exp_sums + row * max_num_partitions;
-    const int slot = tid / LPP, dl = tid % LPP;
-    const float *base = tmp_out + row * (long)max_num_partitions * head_dim + chunk * kReduceChunk + dl * 4;
 
     float m = -INFINITY, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = slot; p0 < n; p0 += SLOTS * kReduceUnroll) {
-        float mv[kReduceUnroll], ev[kReduceUnroll];
-        f32x4 v[kReduceUnroll];
+    for (int p0 = slot;; p0 += SLOTS * kReduceUnroll) {
 #pragma unroll
         for (int u = 0; u < kReduceUnroll; ++u) {
-            const int p = p0 + u * SLOTS;
-            const bool ok = p < n;
-            mv[u] = ok ? mlr[p] : -INFINITY;
-            ev[u] = ok ? esr[p] : 0.f;
-            v[u] = ok ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < kReduceUnroll; ++u) {
+            if (p0 + u * SLOTS >= n) continue;
             if (mv[u] > m) {  // rescale what was accumulated to the new max
                 const float f = fast_exp2((m - mv[u]) * kLog2e);
                 acc *= f;
                 wsum *= f;
                 m = mv[u];
             }
-            const float w = ev[u] > 0.f ? fast_exp2((mv[u] - m) * kLog2e) * ev[u] : 0.f;
+            const float w = fast_exp2((mv[u] - m) * kLog2e) * ev[u];
             acc[0] = fmaf(w, v[u][0], acc[0]);
             acc[1] = fmaf(w, v[u][1], acc[1]);
             acc[2] = fmaf(w, v[u][2], acc[2]);
             acc[3] = fmaf(w, v[u][3], acc[3]);
             wsum += w;
+        }
+        const int q0 = p0 + SLOTS * kReduceUnroll;
+        if (q0 >= n) break;
+#pragma unroll
+        for (int u = 0; u < kReduceUnroll; ++u) {
+            const int p = q0 + u * SLOTS;
+            const bool ok = p < n;
+            mv[u] = ok ? mlr[p] : -INFINITY;
+            ev[u] = ok ? esr[p] : 0.f;
+            v[u] = ok ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     *reinterpret_cast<f32x4 *>(red + slot * kReduceChunk + dl * 4) = acc;
@@ -498,7 +625,7 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
     DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
                      a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2,
                      a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
-                     a.tmp_out};
+                     a.tmp_out, a.counters};
     dim3 block(kDecodeWaves * 64);
     if (a.partition_size > 0 && a.num_seqs <= kCompactMaxSeqs) {
         static int per_cu = 0;  // resident workgroups per CU for this instantiation

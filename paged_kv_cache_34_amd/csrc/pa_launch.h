@@ -21,6 +21,7 @@ struct DecodeArgs {
     int max_num_partitions;    // row stride of the partial buffers
     uint16_t *out;
     float *max_logits, *exp_sums, *tmp_out;
+    int32_t *counters;         // fused merge counters, or null
     hipStream_t stream;
 };
 

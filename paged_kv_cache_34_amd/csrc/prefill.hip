@@ -9,34 +9,45 @@
 // context.  K/V rows are gathered through the block table as in decode.
 //
 // Work decomposition:
-//   * a workgroup owns 128 (row, head) query slots of one kv head: R = 128 / G
-//     consecutive rows times the G query heads that share the kv head (the
-//     AstrAI page's GQA head packing), so every K/V tile is read once for all
-//     G heads; wave w owns slots 32w .. 32w+31;
-//   * KV is walked in 32-token tiles (two 16-token blocks) up to the last
-//     row's causal limit; K is staged row-major and V transposed in LDS,
-//     double buffered;
-//   * S^T = K Q^T is v_mfma_f32_32x32x16_bf16 with K as the A operand and the
-//     wave's query rows (kept in registers) as the B operand; the accumulator
-//     gives each lane 16 tokens of one query slot, which is exactly the bf16
-//     B operand layout of O^T += V^T P^T, so the probabilities never move
-//     between lanes.  The V^T tile is stored with token bits 2 and 3 swapped so
-//     that the A operand of that product is one 16-byte LDS read;
-//   * online softmax per query slot with a lazy running max (rescale only when
-//     a tile's max exceeds it by more than 2^8), fp32 accumulation.
+//   * a workgroup of NW waves owns NW*32 (row, head) query slots of one kv
+//     head: R = NW*32 / G consecutive rows times the G query heads sharing the
+//     kv head (the AstrAI page's GQA head packing), so every K/V tile is read
+//     once for all of them; wave w owns slots 32w .. 32w+31;
+//   * KV is walked in 32-token tiles up to the last row's causal limit.  Each
+//     thread keeps a ring of DEPTH+1 register tiles (global loads issued DEPTH
+//     tiles ahead); K and V are staged row-major in a double-buffered LDS
+//     tile, one barrier per tile;
+//   * S^T = K Q^T is v_mfma_f32_32x32x16_bf16 with K (from LDS) as the A
+//     operand and the wave's query slots (registers) as B; the accumulator
+//     gives each lane 16 tokens of one slot, which is exactly the bf16 B
+//     operand layout of O^T += V^T P^T on the same instruction.  The V^T A
+//     operand is read from the row-major V tile with ds_read_b64_tr_b16 (two
+//     reads of 4 tokens per 32x16 operand);
+//   * online softmax per slot with a lazy running max (rescale only when a
+//     tile's max exceeds it by more than 2^8), fp32 accumulation.
 #include "pa_common.h"
 #include "pa_launch.h"
 
 namespace pa {
 
 namespace {
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfSlots = kPfWaves * 32;  // (row, head) query slots per workgroup
 constexpr int kKvTile = 32;              // KV tokens per tile
+constexpr int kPfDepth = 3;              // register tiles in flight ahead of the one consumed
 constexpr float kPfTau = 8.0f;
+constexpr int kPfIdsLds = 1024;          // block ids staged in LDS (covers 16,384 tokens)
 
-// storage column of token t (0..31) in the V^T tile: swaps bits 2 and 3.
-__device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float max_xor32_pf(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32_pf(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 }  // namespace
 
 template <int D, int G>
@@ -47,16 +58,17 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     int num_q_heads, int num_kv_heads, int max_blocks_per_seq, float scale_log2,
     uint16_t *__restrict__ out) {
     constexpr int R = kPfSlots / G;        // query rows per workgroup
-    constexpr int KROW = D + 8;            // bf16 per K row in LDS (padded)
-    constexpr int VROW = kKvTile + 8;      // bf16 per V^T row in LDS (padded)
+    constexpr int KROW = D + 8;            // bf16 per staged K row (conflict-free b128 reads)
+    constexpr int VROW = D + 16;           // bf16 per staged V row (conflict-free transposed reads)
     constexpr int NK = D / 16;             // k-steps of S^T
-    constexpr int ND = D / 32;             // 32-row tiles of O^T
+    constexpr int ND = D / 32;             // 32-dim tiles of O^T
     constexpr int CPT = D / 8;             // 16-byte chunks per token row
     constexpr int TPP = kPfWaves * 64 / CPT;  // tokens loaded per pass
-    constexpr int PASSES = kKvTile / TPP;
-    static_assert(kKvTile % TPP == 0, "tile load passes");
+    constexpr int PASSES = (kKvTile + TPP - 1) / TPP;
+    constexpr int DEPTH = D >= 256 ? 1 : kPfDepth;
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKvTile * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VROW];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKvTile * VROW];
+    __shared__ int ids_lds[kPfIdsLds];
 
     const int qtile = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
     const int q0 = cu_seqlens[seq];
@@ -69,7 +81,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     const int kv_end = c + r0 + rows;  // keys [0, kv_end) are visible to some row
     const int ntiles = (kv_end + kKvTile - 1) / kKvTile;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, grp = lane >> 5;
     const int slot = wave * 32 + col;
     const int hq = slot / R, rq = slot % R;          // head within group, row within tile
@@ -100,37 +113,51 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     const long tile_elems = 16L * D;
     const long blk_stride = (long)num_kv_heads * tile_elems;
     const int ld_tok = tid / CPT, ld_chunk = tid % CPT;
+    // the block ids this workgroup walks, staged once (no table read in the loop)
+    const int nblk = (kv_end + 15) / 16;
+    for (int b = tid; b < min(nblk, kPfIdsLds); b += kPfWaves * 64) ids_lds[b] = bt_row[b];
+    __syncthreads();
 
-    u32x4 kreg[PASSES], vreg[PASSES];
-    auto load_regs = [&](int tt) {
+    // Tile tt's rows for this thread (one 16-byte chunk of token ps*TPP + ld_tok).
+    // Only tokens below kv_end are real: their block ids are the staged ones
+    // (or, past the staged range, read from the table).  Every other load --
+    // the rest of the last tile, tiles past the last -- reads one fixed line at
+    // the start of the cache, so the loads stay unconditional; their values
+    // are replaced by zeros.
+    auto load_regs = [&](int tt, u32x4 (&kr)[PASSES], u32x4 (&vr)[PASSES]) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
-            const int t = tt * kKvTile + ps * TPP + ld_tok;
-            if (t < L) {
-                const long phys = bt_row[t >> 4];
-                const long off = phys * blk_stride + kvh * tile_elems + (t & 15) * D + ld_chunk * 8;
-                kreg[ps] = load_u32x4(k_cache + off);
-                vreg[ps] = load_u32x4(v_cache + off);
-            } else {
-                kreg[ps] = u32x4{0u, 0u, 0u, 0u};
-                vreg[ps] = u32x4{0u, 0u, 0u, 0u};
+            const int tl = ps * TPP + ld_tok;  // token within the tile
+            const int t = tt * kKvTile + tl;
+            const bool ok = tl < kKvTile && t < kv_end;
+            const int tc = ok ? t : 0;
+            const int b = tc >> 4;
+            long off = ld_chunk * 8;
+            if (ok) {
+                const long phys = b < kPfIdsLds ? ids_lds[b] : bt_row[b];
+                off += phys * blk_stride + kvh * tile_elems + (tc & 15) * D;
+            }
+            const u32x4 kv = load_u32x4(k_cache + off);
+            const u32x4 vv = load_u32x4(v_cache + off);
+            kr[ps] = ok ? kv : u32x4{0u, 0u, 0u, 0u};
+            vr[ps] = ok ? vv : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_lds = [&](int buf, const u32x4 (&kr)[PASSES], const u32x4 (&vr)[PASSES]) {
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int tl = ps * TPP + ld_tok;
+            if (tl < kKvTile) {
+                *reinterpret_cast<u32x4 *>(&k_lds[buf][tl * KROW + ld_chunk * 8]) = kr[ps];
+                *reinterpret_cast<u32x4 *>(&v_lds[buf][tl * VROW + ld_chunk * 8]) = vr[ps];
             }
         }
     };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int ps = 0; ps < PASSES; ++ps) {
-            const int t = ps * TPP + ld_tok;
-            *reinterpret_cast<u32x4 *>(&k_lds[buf][t * KROW + ld_chunk * 8]) = kreg[ps];
-            const int pos = vt_pos(t);
-            uint16_t *vt = &v_lds[buf][(ld_chunk * 8) * VROW + pos];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                vt[(2 * k) * VROW] = (uint16_t)(vreg[ps][k] & 0xffffu);
-                vt[(2 * k + 1) * VROW] = (uint16_t)(vreg[ps][k] >> 16);
-            }
-        }
-    };
+
+    // transposed-read lane address pieces (16-lane group gamma, lane rho in it)
+    const int rho = lane & 15, gamma = lane >> 4;
+    const int vt_row = 4 * (gamma >> 1) + (rho >> 2);                 // + 16 ks + 8 h
+    const int vt_col = 16 * (gamma & 1) + 4 * (rho & 3);              // + 32 dt
 
     auto compute = [&](int tt, int buf) {
         f32x16 s;
@@ -152,17 +179,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
             s[i] = (t <= limit) ? s[i] * scale_log2 : -INFINITY;
             bm = fmaxf(bm, s[i]);
         }
-        bm = fmaxf(bm, xor_lane(bm, 32));
-        const bool need = bm > m_run + kPfTau;
-        if (__any(need)) {
+        bm = max_xor32_pf(bm);
+        if (__any(bm > m_run + kPfTau)) {
             const float mn = fmaxf(m_run, bm);
             const float al = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
             m_run = mn;
             l_run *= al;
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[dt][i] *= al;
+            for (int dt = 0; dt < ND; ++dt) o[dt] *= al;
         }
         u32x4 pk[2];
         float ls = 0.f;
@@ -177,12 +201,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
             }
         }
         l_run += ls;
+        const uint16_t *vl = &v_lds[buf][0];
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-            const uint16_t *vl = &v_lds[buf][(dt * 32 + col) * VROW + 8 * grp];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 va = *reinterpret_cast<const u32x4 *>(vl + ks * 16);
+                // A operand: V[16 ks + 8 h + 4 (lane/32) + 0..3][dim lane%32 + 32 dt], h = 0, 1
+                const uint16_t *a0 = vl + (16 * ks + vt_row) * VROW + 32 * dt + vt_col;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)(a0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)(a0 + 8 * VROW));
+                const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                  __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
                                                                 __builtin_bit_cast(bf16x8, pk[ks]), o[dt],
                                                                 0, 0, 0);
@@ -190,18 +221,28 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         }
     };
 
-    load_regs(0);
-    store_lds(0);
+    // software pipeline: ring of DEPTH+1 register tiles, double-buffered LDS
+    u32x4 kreg[DEPTH + 1][PASSES], vreg[DEPTH + 1][PASSES];
+#pragma unroll
+    for (int d = 0; d <= DEPTH; ++d) load_regs(d, kreg[d], vreg[d]);
+    store_lds(0, kreg[0], vreg[0]);
     __syncthreads();
-    for (int tt = 0; tt < ntiles; ++tt) {
-        const int buf = tt & 1;
-        if (tt + 1 < ntiles) load_regs(tt + 1);
-        compute(tt, buf);
-        if (tt + 1 < ntiles) store_lds(buf ^ 1);
-        __syncthreads();
+    for (int t0 = 0; t0 < ntiles; t0 += DEPTH + 1) {
+#pragma unroll
+        for (int u = 0; u <= DEPTH; ++u) {
+            const int tt = t0 + u;
+            if (tt < ntiles) {
+                compute(tt, tt & 1);
+                // tile tt+1 (in ring slot u+1) goes to the other LDS buffer,
+                // then slot u is refilled with tile tt + DEPTH + 1
+                store_lds((tt + 1) & 1, kreg[(u + 1) % (DEPTH + 1)], vreg[(u + 1) % (DEPTH + 1)]);
+                load_regs(tt + DEPTH + 1, kreg[u], vreg[u]);
+                __syncthreads();
+            }
+        }
     }
 
-    const float l_tot = l_run + xor_lane(l_run, 32);
+    const float l_tot = sum_xor32_pf(l_run);
     if (q_ok) {
         const float inv = 1.f / l_tot;
         uint16_t *orow = out + ((long)(q0 + r0 + rq) * num_q_heads + kvh * G + hq) * D;

@@ -23,7 +23,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = pa.declared_functions()
     assert set(names) == {
-        "paged_attn_decode", "paged_attn_decode_reduce", "paged_attn_prefill_ragged",
+        "paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
+        "paged_attn_prefill_ragged",
         "paged_attn_num_partitions", "paged_attn_choose_partition_size",
         "paged_attn_prefill_tile_map", "paged_attn_status_string"} | (
         set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
@@ -152,4 +153,25 @@ def test_prefill_validation(lib, over, status):
     st = lib.paged_attn_prefill_ragged(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["cu"], a["S"],
                                        a["total_q"], a["max_q"], a["Hq"], a["Hkv"], a["D"], a["bs"],
                                        a["nb"], a["mbps"], a["scale"], a["out"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cnt=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(out=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(ml=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(P=0), pa.PA_ERR_BAD_SHAPE),
+    (dict(P=16, NP=6), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 2), pa.PA_ERR_ALIGNMENT),
+    (dict(S=0), pa.PA_OK),
+])
+def test_fused_decode_validation(lib, over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=4, Hkv=1, D=64, bs=16, nb=16,
+             mbps=7, scale=0.125, P=16, out=FAKE, ml=FAKE, es=FAKE, to=FAKE, NP=7, cnt=FAKE)
+    a.update(over)
+    st = lib.paged_attn_decode_fused(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["S"], a["Hq"],
+                                     a["Hkv"], a["D"], a["bs"], a["nb"], a["mbps"], a["scale"],
+                                     a["P"], a["out"], a["ml"], a["es"], a["to"], a["NP"], a["cnt"],
+                                     None)
     assert st == status

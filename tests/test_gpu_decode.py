@@ -220,3 +220,41 @@ def test_many_sequences_use_the_grid_path(orc):
     lens = rng.integers(1, 300, size=1100)
     case = workloads.build_case("many_seqs", 308, lens, 8, 2, 64)
     check_case(orc, case, partitions=(0, 64), what="1100 sequences")
+
+
+def run_fused(dev, P, ws=None):
+    t = torch()
+    c = dev.case
+    npart = pa.paged_attn_num_partitions(c.max_blocks_per_seq, c.block_size, P)
+    if ws is None:
+        ws = pa.DecodeWorkspace(c.num_seqs, c.num_q_heads, c.head_dim, npart, "cuda",
+                                num_kv_heads=c.num_kv_heads)
+    out = t.full_like(dev.q, float("nan"))
+    pa.paged_attn_decode_fused(dev.q, dev.k, dev.v, dev.bt, dev.sl, float(c.scale), P, out,
+                               ws.max_logits, ws.exp_sums, ws.tmp_out, ws.counters)
+    t.cuda.synchronize()
+    return out, ws
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 16), ("tiny", 48), ("edges", 512), ("edges", 256),
+                                    ("llama3", 512), ("ragged", 1024), ("many", 64)])
+def test_fused_merge(orc, name, P):
+    if name == "tiny":
+        case = workloads.tiny_decode()
+    elif name == "edges":
+        case = workloads.build_case("fused_edges", 320, EDGE_LENS, 12, 2, 128)
+    elif name == "llama3":
+        case = workloads.llama3_8b_decode()
+    elif name == "ragged":
+        case = workloads.large_ragged_decode()
+    else:
+        rng = np.random.default_rng(321)
+        case = workloads.build_case("fused_many", 321, rng.integers(1, 400, size=1100), 8, 2, 64)
+    dev = Dev(case)
+    ref = orc.decode_case(case)
+    announce(f"fused merge {name} P={P} S={case.num_seqs}")
+    out, ws = run_fused(dev, P)
+    assert_out_close(bf16_host_f64(out), ref, f"fused {name} P={P}")
+    assert int(ws.counters.abs().sum().item()) == 0, "arrival counters must be left at zero"
+    out2, _ = run_fused(dev, P, ws)  # the same workspace again
+    assert np.array_equal(bf16_bits_host(out), bf16_bits_host(out2))
