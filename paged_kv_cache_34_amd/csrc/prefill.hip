@@ -39,6 +39,8 @@ constexpr float kPfTau = 8.0f;
 constexpr int kPfIdsLds = 1024;          // block ids staged in LDS (covers 16,384 tokens)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_pf __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_pf __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float max_xor32_pf(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -170,14 +172,24 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
                                                         __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
         }
-        // lane holds tokens (i/4)*8 + 4*grp + i%4 of this tile for query slot `col`
+        // lane holds tokens (i/4)*8 + 4*grp + i%4 of this tile for query slot `col`;
+        // only tiles reaching past the first row's causal limit (or the end
+        // of the visible keys) need the mask
         const int tbase = tt * kKvTile + 4 * grp;
         float bm = -INFINITY;
+        if (tt * kKvTile + kKvTile - 1 > c + r0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = tbase + (i >> 2) * 8 + (i & 3);
-            s[i] = (t <= limit) ? s[i] * scale_log2 : -INFINITY;
-            bm = fmaxf(bm, s[i]);
+            for (int i = 0; i < 16; ++i) {
+                const int t = tbase + (i >> 2) * 8 + (i & 3);
+                s[i] = (t <= limit) ? s[i] * scale_log2 : -INFINITY;
+                bm = fmaxf(bm, s[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] *= scale_log2;
+                bm = fmaxf(bm, s[i]);
+            }
         }
         bm = max_xor32_pf(bm);
         if (__any(bm > m_run + kPfTau)) {
@@ -188,16 +200,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) o[dt] *= al;
         }
+        // a slot that has seen no visible key yet keeps m_run = -inf; its
+        // probabilities are zero (exp2(-inf) after shifting by a finite 0)
+        const float msh = (m_run == -INFINITY) ? 0.f : m_run;
         u32x4 pk[2];
         float ls = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float a = (m_run == -INFINITY) ? 0.f : fast_exp2(s[8 * h + 2 * k] - m_run);
-                const float b = (m_run == -INFINITY) ? 0.f : fast_exp2(s[8 * h + 2 * k + 1] - m_run);
+                const float a = fast_exp2(s[8 * h + 2 * k] - msh);
+                const float b = fast_exp2(s[8 * h + 2 * k + 1] - msh);
                 ls += a + b;
-                pk[h][k] = pack_bf16x2(a, b);
+                pk[h][k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_pf{a, b}, bf16x2_pf));
             }
         }
         l_run += ls;
