@@ -46,7 +46,8 @@ enum paged_attn_status {
     PA_ERR_BAD_SHAPE = 2,     /* non-positive size, H_q % H_kv, partition size, buffer too small */
     PA_ERR_UNSUPPORTED = 3,   /* head_dim, block_size or GQA group outside the supported set */
     PA_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
-    PA_ERR_ALIGNMENT = 5      /* a bf16 / fp32 tensor pointer is not 16-byte aligned */
+    PA_ERR_ALIGNMENT = 5,     /* a bf16 / fp32 tensor pointer is not 16-byte aligned */
+    PA_ERR_BAD_VALUE = 6      /* scale is not a positive finite number */
 };
 
 /*
@@ -69,6 +70,8 @@ enum paged_attn_status {
  *   max_num_partitions must be >= paged_attn_num_partitions(max_blocks_per_seq,
  *   block_size, partition_size).
  * A sequence with seq_lens[s] == 0 gets zeros (single pass) / no partials.
+ * scale must be positive and finite (PA_ERR_BAD_VALUE otherwise), as for
+ * every entry point that takes it.
  * num_seqs == 0 is a no-op returning PA_OK.
  */
 int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -28,6 +28,7 @@ PA_ERR_BAD_SHAPE = 2
 PA_ERR_UNSUPPORTED = 3
 PA_ERR_LAUNCH = 4
 PA_ERR_ALIGNMENT = 5
+PA_ERR_BAD_VALUE = 6
 
 
 class PagedAttnError(RuntimeError):

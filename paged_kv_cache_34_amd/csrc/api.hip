@@ -39,6 +39,10 @@ int check_common(const void *q, const void *k_cache, const void *v_cache,
 
 float log2e_scaled(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
+// The softmax scale must be a positive finite number (the kernels take the
+// maximum of the raw scores as the maximum of the scaled ones).
+bool scale_ok(float scale) { return scale > 0.f && __builtin_isfinite(scale); }
+
 }  // namespace
 
 extern "C" {
@@ -51,6 +55,7 @@ const char *paged_attn_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "unsupported configuration";
         case PA_ERR_LAUNCH: return "kernel launch failed";
         case PA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+        case PA_ERR_BAD_VALUE: return "scale must be positive and finite";
         default: return "unknown status";
     }
 }
@@ -111,6 +116,7 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
     int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
     if (st != PA_OK) return st;
+    if (!scale_ok(scale)) return PA_ERR_BAD_VALUE;
     if (partition_size < 0 || partition_size % kBlockSize != 0) return PA_ERR_BAD_SHAPE;
     int nparts = 1;
     if (partition_size == 0 || counters) {
@@ -213,6 +219,7 @@ int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_
                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
     if (st != PA_OK) return st;
     if (!cu_seqlens || !out) return PA_ERR_NULL_POINTER;
+    if (!scale_ok(scale)) return PA_ERR_BAD_VALUE;
     if (total_q < 0 || max_q_len < 0) return PA_ERR_BAD_SHAPE;
     if (!aligned16(out)) return PA_ERR_ALIGNMENT;
     if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;

@@ -112,67 +112,101 @@ __device__ __forceinline__ float load_partial(float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Block ids of the first 64 tiles a wave of the workgroup will take in the
-// item (one per lane), so that a persistent workgroup can fetch them for its
-// next item while it still works on the current one.
+// A work item as one wave of the workgroup sees it: partition `part` of kv
+// head `kvh` of sequence `seq` (the whole sequence when partition_size == 0;
+// `L` = seq_lens[seq]).  The wave takes the item's 16-token blocks wave,
+// wave + NW, ...; `ids` holds the block ids of its first 64 (one per lane).
+struct DecodeItem {
+    int seq, kvh, part, L;
+    int t_end, b_begin, my_nb, ids;
+};
+
 template <int NW>
-__device__ __forceinline__ int item_first_ids(const DecodeParams &prm, int seq, int part, int L,
-                                              int wave, int lane) {
+__device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq, int kvh, int part,
+                                                int L, int wave, int lane) {
+    DecodeItem it;
+    L = __builtin_amdgcn_readfirstlane(L);  // uniform (the compiler cannot see it when L comes from LDS)
     const int P = prm.partition_size;
     const int t_begin = P ? part * P : 0;
-    const int t_end = P ? min(L, t_begin + P) : L;
-    const int b_begin = t_begin / kBlock;
-    const int nb = (t_end + kBlock - 1) / kBlock - b_begin;
-    const int my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
-    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + b_begin + wave;
-    return (lane < min(64, my_nb)) ? bt_row[NW * lane] : 0;
+    it.seq = seq;
+    it.kvh = kvh;
+    it.part = part;
+    it.L = L;
+    it.t_end = P ? min(L, t_begin + P) : L;
+    it.b_begin = t_begin / kBlock;
+    const int nb = (it.t_end + kBlock - 1) / kBlock - it.b_begin;
+    it.my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + it.b_begin + wave;
+    it.ids = (lane < min(64, it.my_nb)) ? bt_row[NW * lane] : 0;
+    return it;
 }
 
-// `L` is seq_lens[seq]; `ids0` the item's first block ids (item_first_ids).
-template <int D, int G, int NW, int DEPTH>
-__device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, int kvh, int part,
-                                            int L, int ids0, float *lds) {
+// Workgroup barrier for LDS traffic only: unlike __syncthreads it does not
+// wait for the wave's outstanding global loads, so prefetched tiles stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Processes item `it` with the NW waves of the calling workgroup; `lds` is
+// the workgroup's scratch (DecodeShape floats).  `qb` (the item's query rows)
+// and the ring `kbuf`/`vbuf` (its first DEPTH tiles, tile j in slot j) are
+// either loaded here (`primed` false) or were issued by the previous item.
+// When `has_next`, the item issues the same for `nx` before its epilogue, so
+// the next item's first loads are in flight while this one merges its waves.
+// ONE_CHUNK: the caller guarantees at most 64 tiles per wave (NW * 1024
+// tokens per item), so the block ids are never reloaded inside the item.
+//
+// Per 16-token tile a wave computes, with the MFMA lane layouts
+// (col = lane % 16, grp = lane / 16):
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = K tile straight from HBM,
+//                  lane: token col, 16-byte chunk 4j + grp; B = the query rows)
+//                 -> lane holds scores of head col for tokens 4 grp + i;
+//   online softmax per head (block max over the 4 lane groups with permlane
+//   swaps, lazy running max);
+//   O^T += V^T P^T (v_mfma_f32_16x16x16_bf16; A = V^T read from the staged
+//                  row-major V tile with ds_read_b64_tr_b16, B = the lane's own
+//                  probabilities, split into bf16 high and low parts so the
+//                  product keeps ~16 mantissa bits) -> lane holds dims
+//                  16 dt + 4 grp + i of head col.
+// Lanes with col >= G carry a copy of head 0; their results are never stored.
+template <int D, int G, int NW, int DEPTH, bool ONE_CHUNK>
+__device__ __forceinline__ void decode_item(const DecodeParams &prm, const DecodeItem &it,
+                                            const DecodeItem &nx, bool has_next, bool primed,
+                                            u32x4 (&qb)[D / 32], u32x4 (&kbuf)[DEPTH + 1][D / 32],
+                                            u32x4 (&vbuf)[DEPTH + 1][D / 32], float *lds) {
     using S = DecodeShape<D, G, NW>;
     constexpr int NJ = S::NJ, NDT = S::NDT, LPT = S::LPT, TPI = S::TPI, VROW = S::VROW;
-    const uint16_t *__restrict__ q = prm.q;
     const int num_q_heads = prm.num_q_heads;
     const int partition_size = prm.partition_size, max_num_partitions = prm.max_num_partitions;
     const float scale_log2 = prm.scale_log2;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    // (the item fields are wave-uniform; say so, since values carried around
+    // the persistent loop may sit in vector registers)
+    const int seq = __builtin_amdgcn_readfirstlane(it.seq), kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+    const int part = __builtin_amdgcn_readfirstlane(it.part), L = __builtin_amdgcn_readfirstlane(it.L);
+    const int t_end = __builtin_amdgcn_readfirstlane(it.t_end);
+    const int b_begin = __builtin_amdgcn_readfirstlane(it.b_begin);
+    const int my_nb = __builtin_amdgcn_readfirstlane(it.my_nb);
+    const int nx_kvh = __builtin_amdgcn_readfirstlane(nx.kvh);
+    const int nx_nb = __builtin_amdgcn_readfirstlane(nx.my_nb);
     const int h0 = kvh * G;
-    const int t_begin = partition_size ? part * partition_size : 0;
-    if (t_begin >= L) {
-        if (partition_size == 0) {  // empty sequence, single pass: zeros
-            uint16_t *o = prm.out + ((long)seq * num_q_heads + h0) * D;
-            for (int e = tid; e < G * D; e += NW * 64) o[e] = 0;
-        }
-        return;
-    }
-    const int t_end = partition_size ? min(L, t_begin + partition_size) : L;
-    const int b_begin = t_begin / kBlock;
-    const int nb = (t_end + kBlock - 1) / kBlock - b_begin;
-    const int my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
-
     const int col = lane & 15, grp = lane >> 4;
     const int vcol = lane % LPT, vrow = lane / LPT;
 
     // query rows as the B operand of S^T: lane holds q[head col][chunk 4j + grp]
-    u32x4 qb[NJ];
-    {
-        const uint16_t *qrow = q + ((long)seq * num_q_heads + h0 + (col < G ? col : 0)) * D;
+    auto load_q = [&](int s, int g) {
+        const uint16_t *qrow = prm.q + ((long)s * num_q_heads + g * G + (col < G ? col : 0)) * D;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const u32x4 v = load_u32x4(qrow + (4 * j + grp) * 8);
-            qb[j] = (col < G) ? v : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
+        for (int j = 0; j < NJ; ++j) qb[j] = load_u32x4(qrow + (4 * j + grp) * 8);
+    };
 
     const long tile = (long)kBlock * D;
     const long blk_stride = (long)prm.num_kv_heads * tile;
-    const uint16_t *kv_k = prm.k_cache + kvh * tile;
-    const uint16_t *kv_v = prm.v_cache + kvh * tile;
+    const uint16_t *kv_k = prm.k_cache + kvh * tile, *kv_v = prm.v_cache + kvh * tile;
+    const uint16_t *nx_k = prm.k_cache + nx_kvh * tile, *nx_v = prm.v_cache + nx_kvh * tile;
     const int k_voff = (col * D + grp * 8) * 2;     // bytes within a tile
     const int v_voff = (vrow * D + vcol * 8) * 2;
     const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + b_begin + wave;
@@ -187,20 +221,30 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
     for (int dt = 0; dt < NDT; ++dt) oT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, m_ex = -INFINITY, l_run = 0.f;
 
-    // Loads tile slot `i` of the current 64-tile chunk with buffer loads whose
-    // descriptor covers exactly that tile; slots past the chunk get an empty
-    // descriptor, so their loads return zeros without touching memory and the
-    // loads stay unconditional (the compiler's wait counts stay exact).
-    auto load_tile = [&](int ids, int i, int n, u32x4 (&kr)[NJ], u32x4 (&vr)[NJ]) {
-        const bool ok = i < n;
-        const long phys = __builtin_amdgcn_readlane(ids, ok ? i : 0);
-        const int bytes = ok ? (int)(tile * 2) : 0;
-        const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)(kv_k + phys * blk_stride), 0, bytes, kBufferFlags);
-        const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(kv_v + phys * blk_stride), 0, bytes, kBufferFlags);
+    // Issues tile j of the current chunk (n tiles, block ids `ids` one per
+    // lane) into a ring slot with buffer loads whose descriptor covers exactly
+    // that tile.  In the item's last chunk the tiles past its end are the next
+    // item's first tiles, counted from the first multiple of DEPTH + 1 at or
+    // after n so that they land in ring slots 0, 1, ...; any other slot gets an
+    // empty descriptor, whose loads return zeros without touching memory.  All
+    // choices are wave-uniform and the loads unconditional, so the compiler's
+    // wait counts stay exact.
+    auto load_tile = [&](int ids, int j, int n, bool last, u32x4 (&kr)[NJ], u32x4 (&vr)[NJ]) {
+        const int base = (n + DEPTH) / (DEPTH + 1) * (DEPTH + 1);
+        const int jn = j - base;
+        const bool cur = j < n;
+        const bool nxt = !cur && last && has_next && jn >= 0 && jn < min(64, nx_nb);
+        const long phys = cur ? __builtin_amdgcn_readlane(ids, j)
+                              : __builtin_amdgcn_readlane(nx.ids, nxt ? jn : 0);
+        const int bytes = (cur || nxt) ? (int)(tile * 2) : 0;
+        const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? kv_k : nx_k) + phys * blk_stride),
+                                                           0, bytes, kBufferFlags);
+        const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? kv_v : nx_v) + phys * blk_stride),
+                                                           0, bytes, kBufferFlags);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            kr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + j * 64, 0, 0));
-            vr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + j * TPI * D * 2, 0, 0));
+        for (int j2 = 0; j2 < NJ; ++j2) {
+            kr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + j2 * 64, 0, 0));
+            vr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + j2 * TPI * D * 2, 0, 0));
         }
     };
 
@@ -255,28 +299,58 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
         wave_lds_sync();
     };
 
+    if (!primed) {
+        load_q(seq, kvh);
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_tile(it.ids, d, min(64, my_nb), my_nb <= 64, kbuf[d], vbuf[d]);
+    }
+
     // Tiles are processed in chunks of 64 whose block ids sit one per lane;
     // within a chunk a ring of DEPTH + 1 register tiles keeps tile i + DEPTH
     // in flight while tile i is consumed.
-    for (int c0 = 0; c0 < my_nb; c0 += 64) {
-        const int n = min(64, my_nb - c0);
-        const int ids = c0 == 0 ? ids0 : ((lane < n) ? bt_row[NW * (c0 + lane)] : 0);
-        u32x4 kbuf[DEPTH + 1][NJ], vbuf[DEPTH + 1][NJ];
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) load_tile(ids, d, n, kbuf[d], vbuf[d]);
+    auto run_chunk = [&](int ids, int c0, int n, bool last) {
         for (int i = 0; i < n; i += DEPTH + 1) {
 #pragma unroll
             for (int u = 0; u <= DEPTH; ++u) {
-                load_tile(ids, i + u + DEPTH, n, kbuf[(u + DEPTH) % (DEPTH + 1)],
+                load_tile(ids, i + u + DEPTH, n, last, kbuf[(u + DEPTH) % (DEPTH + 1)],
                           vbuf[(u + DEPTH) % (DEPTH + 1)]);
                 if (i + u < n) compute_tile(c0 + i + u, kbuf[u], vbuf[u]);
             }
         }
+    };
+    if (ONE_CHUNK) {
+        run_chunk(it.ids, 0, my_nb, true);
+    } else {
+        for (int c0 = 0; c0 < my_nb; c0 += 64) {
+            const int n = min(64, my_nb - c0);
+            const bool last = c0 + 64 >= my_nb;
+            const int ids = c0 == 0 ? it.ids : ((lane < n) ? bt_row[NW * (c0 + lane)] : 0);
+            if (c0 > 0) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) load_tile(ids, d, n, last, kbuf[d], vbuf[d]);
+            }
+            run_chunk(ids, c0, n, last);
+        }
+    }
+    if (has_next) {
+        // a wave that streamed nothing has not issued the next item's tiles yet
+        if (my_nb == 0) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) load_tile(0, d, 0, true, kbuf[d], vbuf[d]);
+        }
+        load_q(__builtin_amdgcn_readfirstlane(nx.seq), nx_kvh);
     }
 
     // ---- per-wave totals -------------------------------------------------
+    // (the fused merge needs full barriers; otherwise LDS-only barriers keep
+    // the next item's loads in flight)
+    const bool fused = prm.counters != nullptr;
+    auto wg_sync = [&]() {
+        if (fused) __syncthreads();
+        else lds_barrier();
+    };
     l_run = sum_xor32(sum_xor16(l_run));
-    __syncthreads();  // every wave is done with its staging tile before the buffer is reused
+    wg_sync();  // every wave is done with its staging tile before the buffer is reused
     float *red = lds;                      // [NW][G][D]
     float *st_m = lds + S::MAIN_FLOATS;    // [NW][16] running max (log2 units)
     float *st_x = st_m + NW * 16;          // [NW][16] exact max (log2 units)
@@ -291,7 +365,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
             st_l[wave * 16 + col] = l_run;
         }
     }
-    __syncthreads();
+    wg_sync();
 
     // ---- merge the waves (fixed order) and write ---------------------------
     // The item writes bf16 output directly when it is the whole sequence
@@ -299,7 +373,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
     // partial record.
     const long row0 = (long)seq * num_q_heads + h0;
     const int nparts = partition_size ? (L + partition_size - 1) / partition_size : 1;
-    const bool fused = prm.counters != nullptr;
     const bool direct = partition_size == 0 || (fused && nparts == 1);
     for (int e = tid; e < G * D; e += NW * 64) {
         const int h = e / D, d = e % D;
@@ -379,7 +452,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, int seq, in
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    __syncthreads();  // the next item of a persistent workgroup reuses `lds`
+    wg_sync();  // the next item of a persistent workgroup reuses `lds`
 }
 
 // One workgroup per (partition, kv head, sequence); workgroups whose partition
@@ -390,16 +463,26 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
     const int seq = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
     const int L = prm.seq_lens[seq];
+    const int P = prm.partition_size;
+    if ((P ? part * P : 0) >= L) {
+        if (P == 0) {  // empty sequence, single pass: zeros
+            uint16_t *o = prm.out + ((long)seq * prm.num_q_heads + kvh * G) * D;
+            for (int e = threadIdx.x; e < G * D; e += NW * 64) o[e] = 0;
+        }
+        return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ids0 = item_first_ids<NW>(prm, seq, part, L, wave, threadIdx.x & 63);
-    decode_item<D, G, NW, DEPTH>(prm, seq, kvh, part, L, ids0, lds);
+    const DecodeItem it = make_item<NW>(prm, seq, kvh, part, L, wave, threadIdx.x & 63);
+    u32x4 qb[D / 32], kbuf[DEPTH + 1][D / 32], vbuf[DEPTH + 1][D / 32];
+    decode_item<D, G, NW, DEPTH, false>(prm, it, it, false, false, qb, kbuf, vbuf, lds);
 }
 
 // Compact persistent split-KV: every workgroup first builds, in LDS, the
 // prefix over sequences of their item counts H_kv * ceil(L / P) (items are
 // ordered sequence, kv head, partition), then takes items blockIdx.x,
 // blockIdx.x + gridDim.x, ...  Only partitions that exist are ever visited, so
-// no workgroup is spent on the empty tail of an upper-bound grid.
+// no workgroup is spent on the empty tail of an upper-bound grid.  Each item
+// issues the next one's query rows and first K/V tiles before its epilogue.
 constexpr int kCompactMaxSeqs = 1024;
 
 template <int D, int G, int NW, int DEPTH>
@@ -448,43 +531,41 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     if (tid == 0) pref[0] = 0;
     __syncthreads();
 
-    const int total = pref[nseq];
-    // item -> (sequence, kv head, partition): largest s with pref[s] <= item
-    auto locate = [&](int item, int &seq, int &kvh, int &part) {
+    const int total = __builtin_amdgcn_readfirstlane(pref[nseq]);  // uniform loop bound
+    // item -> its description: (sequence, kv head, partition) is found as the
+    // largest s with pref[s] <= item, then the rest within the sequence
+    auto locate = [&](int item) {
         int lo = 0, hi = nseq;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (pref[mid] <= item) lo = mid; else hi = mid;
         }
-        seq = __builtin_amdgcn_readfirstlane(lo);
+        const int seq = __builtin_amdgcn_readfirstlane(lo);
         const int np = (pref[seq + 1] - pref[seq]) / hkv;
         const int rr = item - pref[seq];
-        kvh = __builtin_amdgcn_readfirstlane(rr / np);
-        part = __builtin_amdgcn_readfirstlane(rr % np);
+        const int kvh = __builtin_amdgcn_readfirstlane(rr / np);
+        const int part = __builtin_amdgcn_readfirstlane(rr % np);
+        return make_item<NW>(prm, seq, kvh, part, lens[seq], wave, lane);
     };
     int item = blockIdx.x;
     if (item >= total) return;
-    int seq, kvh, part;
-    locate(item, seq, kvh, part);
-    int L = lens[seq];
-    int ids = item_first_ids<NW>(prm, seq, part, L, wave, lane);
+    DecodeItem it = locate(item);
+    // Settle the first item's block-id load here: the wait the compiler would
+    // otherwise place at the top of the item loop (where it would also drain
+    // the prefetched loads of every later item) becomes a no-op.
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 qb[D / 32], kbuf[DEPTH + 1][D / 32], vbuf[DEPTH + 1][D / 32];
+    bool primed = false;
     for (;;) {
         // the next item's block ids are fetched while this one streams
         const int next = item + gridDim.x;
-        int nseq_, nkvh, npart, nL = 0, nids = 0;
-        if (next < total) {
-            locate(next, nseq_, nkvh, npart);
-            nL = lens[nseq_];
-            nids = item_first_ids<NW>(prm, nseq_, npart, nL, wave, lane);
-        }
-        decode_item<D, G, NW, DEPTH>(prm, seq, kvh, part, L, ids, lds);
-        if (next >= total) break;
+        const bool has_next = next < total;
+        const DecodeItem nx = has_next ? locate(next) : it;
+        decode_item<D, G, NW, DEPTH, true>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
+        if (!has_next) break;
         item = next;
-        seq = nseq_;
-        kvh = nkvh;
-        part = npart;
-        L = nL;
-        ids = nids;
+        it = nx;
+        primed = true;
     }
 }
 
@@ -627,7 +708,7 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
                      a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
                      a.tmp_out, a.counters};
     dim3 block(kDecodeWaves * 64);
-    if (a.partition_size > 0 && a.num_seqs <= kCompactMaxSeqs) {
+    if (a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock && a.num_seqs <= kCompactMaxSeqs) {
         static int per_cu = 0;  // resident workgroups per CU for this instantiation
         if (per_cu == 0) {
             int n = 0;

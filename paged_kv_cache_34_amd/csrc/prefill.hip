@@ -25,6 +25,8 @@
 //     reads of 4 tokens per 32x16 operand);
 //   * online softmax per slot with a lazy running max (rescale only when a
 //     tile's max exceeds it by more than 2^8), fp32 accumulation.
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -37,6 +39,8 @@ constexpr int kKvTile = 32;              // KV tokens per tile
 constexpr int kPfDepth = 3;              // register tiles in flight ahead of the one consumed
 constexpr float kPfTau = 8.0f;
 constexpr int kPfIdsLds = 1024;          // block ids staged in LDS (covers 16,384 tokens)
+// Fourth word of a raw buffer descriptor on the GFX9 family (32-bit data, no swizzle).
+constexpr int kPfBufferFlags = 0x00020000;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2_pf __attribute__((ext_vector_type(2)));
@@ -61,13 +65,15 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     uint16_t *__restrict__ out) {
     constexpr int R = kPfSlots / G;        // query rows per workgroup
     constexpr int KROW = D + 8;            // bf16 per staged K row (conflict-free b128 reads)
-    constexpr int VROW = D + 16;           // bf16 per staged V row (conflict-free transposed reads)
+    constexpr int VROW = D + 32;           // bf16 per staged V row: the 4 rows x 64 bytes a
+                                           // transposed read takes per 32 lanes hit all 64 banks
     constexpr int NK = D / 16;             // k-steps of S^T
     constexpr int ND = D / 32;             // 32-dim tiles of O^T
     constexpr int CPT = D / 8;             // 16-byte chunks per token row
     constexpr int TPP = kPfWaves * 64 / CPT;  // tokens loaded per pass
     constexpr int PASSES = (kKvTile + TPP - 1) / TPP;
     constexpr int DEPTH = D >= 256 ? 1 : kPfDepth;
+    static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKvTile * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKvTile * VROW];
     __shared__ int ids_lds[kPfIdsLds];
@@ -120,29 +126,31 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     for (int b = tid; b < min(nblk, kPfIdsLds); b += kPfWaves * 64) ids_lds[b] = bt_row[b];
     __syncthreads();
 
-    // Tile tt's rows for this thread (one 16-byte chunk of token ps*TPP + ld_tok).
-    // Only tokens below kv_end are real: their block ids are the staged ones
-    // (or, past the staged range, read from the table).  Every other load --
-    // the rest of the last tile, tiles past the last -- reads one fixed line at
-    // the start of the cache, so the loads stay unconditional; their values
-    // are replaced by zeros.
+    // Tile tt's rows for this thread: one 16-byte chunk of token ps*TPP + ld_tok.
+    // The 512/D tokens a wave loads in one pass lie in one 16-token block, so
+    // the block id and the buffer descriptor are wave-uniform.  The descriptor
+    // covers only the block's rows below kv_end, so the rest of the last tile
+    // and whole tiles past it read as zeros without touching memory, and the
+    // loads stay unconditional.  Block ids come from LDS (staged above) or,
+    // past the staged range, from the table with a scalar load.
+    const int wtok = __builtin_amdgcn_readfirstlane(wave * (64 / CPT));  // wave's first token in a pass
+    const int ld_voff = ((ld_tok & 15) * D + ld_chunk * 8) * 2;          // bytes within a block tile
+    const auto *bt_const = (const __attribute__((address_space(4))) int32_t *)bt_row;
     auto load_regs = [&](int tt, u32x4 (&kr)[PASSES], u32x4 (&vr)[PASSES]) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
-            const int tl = ps * TPP + ld_tok;  // token within the tile
-            const int t = tt * kKvTile + tl;
-            const bool ok = tl < kKvTile && t < kv_end;
-            const int tc = ok ? t : 0;
-            const int b = tc >> 4;
-            long off = ld_chunk * 8;
-            if (ok) {
-                const long phys = b < kPfIdsLds ? ids_lds[b] : bt_row[b];
-                off += phys * blk_stride + kvh * tile_elems + (tc & 15) * D;
-            }
-            const u32x4 kv = load_u32x4(k_cache + off);
-            const u32x4 vv = load_u32x4(v_cache + off);
-            kr[ps] = ok ? kv : u32x4{0u, 0u, 0u, 0u};
-            vr[ps] = ok ? vv : u32x4{0u, 0u, 0u, 0u};
+            const int tl0 = ps * TPP + wtok;   // the wave's first token within the tile
+            const int b = (tt * kKvTile + tl0) >> 4;
+            const int rows = tl0 < kKvTile ? min(max(kv_end - b * 16, 0), 16) : 0;
+            int phys = 0;
+            if (rows > 0) phys = b < kPfIdsLds ? ids_lds[b] : bt_const[b];
+            phys = __builtin_amdgcn_readfirstlane(phys);
+            const long base = (long)phys * blk_stride + kvh * tile_elems;
+            const int bytes = rows * D * 2;
+            const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)(k_cache + base), 0, bytes, kPfBufferFlags);
+            const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(v_cache + base), 0, bytes, kPfBufferFlags);
+            kr[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ld_voff, 0, 0));
+            vr[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ld_voff, 0, 0));
         }
     };
     auto store_lds = [&](int buf, const u32x4 (&kr)[PASSES], const u32x4 (&vr)[PASSES]) {
@@ -174,24 +182,23 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         }
         // lane holds tokens (i/4)*8 + 4*grp + i%4 of this tile for query slot `col`;
         // only tiles reaching past the first row's causal limit (or the end
-        // of the visible keys) need the mask
+        // of the visible keys) need the mask.  With scale > 0 the max of the
+        // raw scores gives the max of the scaled ones, and the scaling folds
+        // into the exponent's FMA below.
         const int tbase = tt * kKvTile + 4 * grp;
-        float bm = -INFINITY;
+        float mr = -INFINITY;
         if (tt * kKvTile + kKvTile - 1 > c + r0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int t = tbase + (i >> 2) * 8 + (i & 3);
-                s[i] = (t <= limit) ? s[i] * scale_log2 : -INFINITY;
-                bm = fmaxf(bm, s[i]);
+                s[i] = (t <= limit) ? s[i] : -INFINITY;
+                mr = fmaxf(mr, s[i]);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[i] *= scale_log2;
-                bm = fmaxf(bm, s[i]);
-            }
+            for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[i]);
         }
-        bm = max_xor32_pf(bm);
+        const float bm = max_xor32_pf(mr) * scale_log2;  // tile max, log2 units
         if (__any(bm > m_run + kPfTau)) {
             const float mn = fmaxf(m_run, bm);
             const float al = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
@@ -209,8 +216,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float a = fast_exp2(s[8 * h + 2 * k] - msh);
-                const float b = fast_exp2(s[8 * h + 2 * k + 1] - msh);
+                const float a = fast_exp2(fmaf(s[8 * h + 2 * k], scale_log2, -msh));
+                const float b = fast_exp2(fmaf(s[8 * h + 2 * k + 1], scale_log2, -msh));
                 ls += a + b;
                 pk[h][k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_pf{a, b}, bf16x2_pf));
             }
@@ -242,20 +249,28 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     for (int d = 0; d <= DEPTH; ++d) load_regs(d, kreg[d], vreg[d]);
     store_lds(0, kreg[0], vreg[0]);
     __syncthreads();
-    for (int t0 = 0; t0 < ntiles; t0 += DEPTH + 1) {
-#pragma unroll
-        for (int u = 0; u <= DEPTH; ++u) {
-            const int tt = t0 + u;
-            if (tt < ntiles) {
-                compute(tt, tt & 1);
-                // tile tt+1 (in ring slot u+1) goes to the other LDS buffer,
-                // then slot u is refilled with tile tt + DEPTH + 1
-                store_lds((tt + 1) & 1, kreg[(u + 1) % (DEPTH + 1)], vreg[(u + 1) % (DEPTH + 1)]);
-                load_regs(tt + DEPTH + 1, kreg[u], vreg[u]);
-                __syncthreads();
-            }
-        }
+    // One step: compute tile tt from LDS; tile tt+1 (ring slot u+1) goes to
+    // the other LDS buffer; slot u is refilled with tile tt + DEPTH + 1.
+    auto step = [&](int tt, auto uc) {
+        constexpr int u = decltype(uc)::value;
+        compute(tt, tt & 1);
+        store_lds((tt + 1) & 1, kreg[(u + 1) % (DEPTH + 1)], vreg[(u + 1) % (DEPTH + 1)]);
+        load_regs(tt + DEPTH + 1, kreg[u], vreg[u]);
+        __syncthreads();
+    };
+    // Full groups of DEPTH + 1 steps have no guards, so the loop's back edge
+    // always comes after the last slot's refill (the compiler's wait counts
+    // for the ring stay exact); the remaining steps follow the loop.
+    int t0 = 0;
+    for (; t0 + DEPTH < ntiles; t0 += DEPTH + 1) {
+        step(t0, std::integral_constant<int, 0>{});
+        if constexpr (DEPTH >= 1) step(t0 + 1, std::integral_constant<int, 1>{});
+        if constexpr (DEPTH >= 2) step(t0 + 2, std::integral_constant<int, 2>{});
+        if constexpr (DEPTH >= 3) step(t0 + 3, std::integral_constant<int, 3>{});
     }
+    if (t0 < ntiles) step(t0, std::integral_constant<int, 0>{});
+    if constexpr (DEPTH >= 2) if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (DEPTH >= 3) if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
 
     const float l_tot = sum_xor32_pf(l_run);
     if (q_ok) {

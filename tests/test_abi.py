@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     assert pa.status_string(0) == "ok"
-    for code in range(1, 6):
+    for code in range(1, 7):
         assert pa.status_string(code) not in ("ok", "unknown status")
     assert pa.status_string(99) == "unknown status"
 
@@ -112,6 +112,10 @@ def decode_call(lib, **over):
     (dict(Hq=34, Hkv=2), pa.PA_ERR_UNSUPPORTED),
     (dict(q=FAKE + 8), pa.PA_ERR_ALIGNMENT),
     (dict(out=FAKE + 2), pa.PA_ERR_ALIGNMENT),
+    (dict(scale=0.0), pa.PA_ERR_BAD_VALUE),
+    (dict(scale=-0.125), pa.PA_ERR_BAD_VALUE),
+    (dict(scale=float("inf")), pa.PA_ERR_BAD_VALUE),
+    (dict(scale=float("nan")), pa.PA_ERR_BAD_VALUE),
     (dict(S=0), pa.PA_OK),
 ])
 def test_decode_validation(lib, over, status):
@@ -143,6 +147,8 @@ def test_reduce_validation(lib, over, status):
     (dict(Hq=8, Hkv=3), pa.PA_ERR_BAD_SHAPE),
     (dict(D=48), pa.PA_ERR_UNSUPPORTED),
     (dict(out=FAKE + 6), pa.PA_ERR_ALIGNMENT),
+    (dict(scale=-1.0), pa.PA_ERR_BAD_VALUE),
+    (dict(scale=float("nan")), pa.PA_ERR_BAD_VALUE),
     (dict(total_q=0, max_q=0), pa.PA_OK),
     (dict(S=0), pa.PA_OK),
 ])
@@ -164,6 +170,7 @@ def test_prefill_validation(lib, over, status):
     (dict(P=16, NP=6), pa.PA_ERR_BAD_SHAPE),
     (dict(D=32), pa.PA_ERR_UNSUPPORTED),
     (dict(out=FAKE + 2), pa.PA_ERR_ALIGNMENT),
+    (dict(scale=0.0), pa.PA_ERR_BAD_VALUE),
     (dict(S=0), pa.PA_OK),
 ])
 def test_fused_decode_validation(lib, over, status):
