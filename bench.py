@@ -290,10 +290,21 @@ def run_prefill(args, pa):
     out = torch.empty_like(d["q"])
     stream = torch.cuda.current_stream()
     scale = float(case.scale)
+    split = args.prefill_form == "split"
+    ws = None
+    if split:
+        ws = pa.PrefillWorkspace(case.num_seqs, case.total_q, case.num_q_heads, case.num_kv_heads,
+                                 case.head_dim, case.max_blocks_per_seq, 16, "cuda")
+        log(f"split-KV prefill, key chunk {ws.kv_chunk}, workspace {ws.buffer.numel() / 1e6:.1f} MB")
 
     def step():
-        pa.paged_attn_prefill_ragged(d["q"], d["k"], d["v"], d["bt"], d["sl"], d["cu"], case.max_q_len,
-                                     scale, out, stream=stream)
+        if split:
+            pa.paged_attn_prefill_ragged_split(d["q"], d["k"], d["v"], d["bt"], d["sl"], d["cu"],
+                                               case.max_q_len, scale, out, workspace=ws.buffer,
+                                               stream=stream)
+        else:
+            pa.paged_attn_prefill_ragged(d["q"], d["k"], d["v"], d["bt"], d["sl"], d["cu"],
+                                         case.max_q_len, scale, out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -318,9 +329,16 @@ def run_prefill(args, pa):
         "data": "synthetic",
         "config": {"workload": "ragged_prefill", "num_seqs": case.num_seqs, "total_q": case.total_q,
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
-                   "head_dim": case.head_dim, "kv_tokens": case.kv_tokens},
+                   "head_dim": case.head_dim, "kv_tokens": case.kv_tokens,
+                   "form": "split-KV" if split else "single pass",
+                   "kv_chunk": ws.kv_chunk if split else 0},
         "kv_gbps": case.kv_bytes / (ms * 1e-3) / 1e9,
-        "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel", "achieved": tflops,
+        # the split form is one API call of two launches (chunks, then merge);
+        # its time is taken over both, so the merge counts against the kernel
+        "roofline": {"bound": "mfma",
+                     "kernel": ("paged_prefill_split_kernel+paged_prefill_merge_kernel" if split
+                                else "paged_prefill_kernel"),
+                     "achieved": tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                      "traffic": counter_traffic("prefill", PREFILL_SOURCE, "ragged_prefill"),
                      "kernel_ms": ms, "algorithmic_flops_per_launch": flops},
@@ -354,6 +372,8 @@ def main():
     ap.add_argument("--merge", default="separate", choices=["fused", "separate"],
                     help="cross-partition merge: a separate kernel (default; faster on MI355X at "
                          "these shapes) or fused into the partition kernel")
+    ap.add_argument("--prefill-form", default="split", choices=["split", "single"],
+                    help="ragged_prefill: split-KV entry point (default) or the single-pass one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

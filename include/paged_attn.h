@@ -137,7 +137,53 @@ int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_
                               int block_size, int num_blocks, int max_blocks_per_seq,
                               float scale, void *out, void *stream);
 
+/*
+ * Ragged paged prefill, split-KV form: the same inputs, rows and output as
+ * paged_attn_prefill_ragged, computed by cutting every (query tile, kv head)
+ * into key chunks of kv_chunk tokens (the BI-V100 design page's partitioning,
+ * section 2 "Level 3", applied to prefill) so that long contexts spread over
+ * the whole GPU.  A persistent grid takes the chunks from a device counter;
+ * rows whose keys all lie in the first chunk are written directly, the others
+ * leave one fp32 partial record (running max, exp-sum, normalized output) per
+ * chunk, merged by a second kernel with the page's combine rule.
+ *   kv_chunk   0 = paged_attn_prefill_chunk_size(...); else a positive
+ *              multiple of 32, at most 8192.
+ *   workspace  device memory, 16-byte aligned, of at least
+ *              paged_attn_prefill_workspace_size(...) bytes for the chunk in
+ *              use.  Its first 8 bytes are two counters that must be zero
+ *              before the first call (clear the buffer once after
+ *              allocation); every completed call leaves them zero.  Calls
+ *              that overlap in time must not share a workspace.
+ * When the chunk list does not fit (more than 1024 sequences or (sequence,
+ * query tile) pairs) or one chunk covers the longest context, the call runs
+ * the single-pass kernel and does not touch the workspace (it may then be
+ * NULL).  Same status codes as paged_attn_prefill_ragged, plus
+ * PA_ERR_BAD_SHAPE for a bad kv_chunk or a workspace that is too small.
+ */
+int paged_attn_prefill_ragged_split(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *seq_lens,
+                                    const int32_t *cu_seqlens, int num_seqs, int total_q,
+                                    int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, int max_blocks_per_seq,
+                                    float scale, int kv_chunk, void *workspace,
+                                    long long workspace_bytes, void *out, void *stream);
+
 /* ---- host-only helpers (no device work) ---------------------------------- */
+
+/* Key chunk the split-KV prefill uses when kv_chunk == 0: about eight chunks
+ * per CU of the current device if every (sequence, query tile) pair had the
+ * longest context, a multiple of 256 in [512, 8192]; 0 when the single pass
+ * is used instead (too many pairs, or one chunk covers the longest context).
+ * The pair count is bounded by ceil(total_q / (256 / G)) + num_seqs. */
+int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
+                                  int max_blocks_per_seq, int block_size);
+
+/* Workspace bytes of paged_attn_prefill_ragged_split for a chunk of kv_chunk
+ * tokens: 256 + 2 * R4 + R4 * head_dim, R4 = total_q * num_q_heads *
+ * ceil(max_blocks_per_seq * block_size / kv_chunk) * 4 bytes, each section
+ * rounded up to 256 bytes; -1 for invalid arguments. */
+long long paged_attn_prefill_workspace_size(int total_q, int num_q_heads, int head_dim,
+                                            int max_blocks_per_seq, int block_size, int kv_chunk);
 
 /* Partition count covering max_blocks_per_seq * block_size tokens; 1 when
  * partition_size == 0; -1 on a bad argument. */

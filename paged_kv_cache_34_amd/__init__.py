@@ -55,13 +55,19 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_decode_fused.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp, _vp]
         lib.paged_attn_decode_reduce.argtypes = [_vp] * 4 + [_i] * 5 + [_vp, _vp]
         lib.paged_attn_prefill_ragged.argtypes = [_vp] * 6 + [_i] * 9 + [ctypes.c_float, _vp, _vp]
+        lib.paged_attn_prefill_ragged_split.argtypes = ([_vp] * 6 + [_i] * 9 + [ctypes.c_float, _i, _vp,
+                                                          ctypes.c_longlong, _vp, _vp])
+        lib.paged_attn_prefill_chunk_size.argtypes = [_i] * 6
+        lib.paged_attn_prefill_workspace_size.argtypes = [_i] * 6
+        lib.paged_attn_prefill_workspace_size.restype = ctypes.c_longlong
         lib.paged_attn_num_partitions.argtypes = [_i, _i, _i]
         lib.paged_attn_choose_partition_size.argtypes = [_i, _i, _i, ctypes.c_long]
         lib.paged_attn_prefill_tile_map.argtypes = [_vp, _i, _i, _vp, _vp, _i]
         lib.paged_attn_status_string.argtypes = [_i]
         lib.paged_attn_status_string.restype = ctypes.c_char_p
         for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
-                   "paged_attn_prefill_ragged",
+                   "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
+                   "paged_attn_prefill_chunk_size",
                    "paged_attn_num_partitions", "paged_attn_choose_partition_size",
                    "paged_attn_prefill_tile_map"):
             getattr(lib, fn).restype = _i
@@ -191,6 +197,61 @@ def paged_attn_prefill_ragged(q, k_cache, v_cache, block_tables, seq_lens, cu_se
         _ptr(cu_seqlens), seq_lens.shape[0], total_q, int(max_q_len), hq, hkv, d, bs, num_blocks,
         block_tables.shape[1], float(scale), _ptr(out), _stream(stream))
     _check("paged_attn_prefill_ragged", st)
+
+
+def paged_attn_prefill_ragged_split(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens,
+                                    max_q_len: int, scale: float, out, workspace=None,
+                                    kv_chunk: int = 0, stream=None) -> None:
+    """Split-KV form of the ragged causal prefill.  `workspace` is a uint8 device
+    tensor of at least paged_attn_prefill_workspace_size(...) bytes whose first
+    8 bytes are zero before the first call (a PrefillWorkspace provides one)."""
+    import torch
+    _want(q, torch.bfloat16, "q")
+    _want(k_cache, torch.bfloat16, "k_cache")
+    _want(v_cache, torch.bfloat16, "v_cache")
+    _want(block_tables, torch.int32, "block_tables")
+    _want(seq_lens, torch.int32, "seq_lens")
+    _want(cu_seqlens, torch.int32, "cu_seqlens")
+    _want(out, torch.bfloat16, "out")
+    _want(workspace, torch.uint8, "workspace")
+    total_q, hq, d = q.shape
+    num_blocks, hkv, bs, _ = k_cache.shape
+    nbytes = 0 if workspace is None else workspace.numel()
+    st = library().paged_attn_prefill_ragged_split(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+        _ptr(cu_seqlens), seq_lens.shape[0], total_q, int(max_q_len), hq, hkv, d, bs, num_blocks,
+        block_tables.shape[1], float(scale), int(kv_chunk), _ptr(workspace), nbytes, _ptr(out),
+        _stream(stream))
+    _check("paged_attn_prefill_ragged_split", st)
+
+
+def paged_attn_prefill_chunk_size(num_seqs: int, total_q: int, num_q_heads: int, num_kv_heads: int,
+                                  max_blocks_per_seq: int, block_size: int) -> int:
+    return int(library().paged_attn_prefill_chunk_size(num_seqs, total_q, num_q_heads, num_kv_heads,
+                                                       max_blocks_per_seq, block_size))
+
+
+def paged_attn_prefill_workspace_size(total_q: int, num_q_heads: int, head_dim: int,
+                                      max_blocks_per_seq: int, block_size: int, kv_chunk: int) -> int:
+    return int(library().paged_attn_prefill_workspace_size(total_q, num_q_heads, head_dim,
+                                                           max_blocks_per_seq, block_size, kv_chunk))
+
+
+class PrefillWorkspace:
+    """Zero-filled device workspace for paged_attn_prefill_ragged_split, sized for
+    the chunk the call will use (kv_chunk, or the automatic choice when 0)."""
+
+    def __init__(self, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                 block_size, device, kv_chunk: int = 0):
+        import torch
+        chunk = int(kv_chunk) or paged_attn_prefill_chunk_size(
+            num_seqs, total_q, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size)
+        self.kv_chunk = chunk
+        nbytes = 256
+        if chunk > 0:
+            nbytes = paged_attn_prefill_workspace_size(total_q, num_q_heads, head_dim,
+                                                       max_blocks_per_seq, block_size, chunk)
+        self.buffer = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def paged_attn_num_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:

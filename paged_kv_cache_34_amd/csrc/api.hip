@@ -43,6 +43,30 @@ float log2e_scaled(float scale) { return (float)((double)scale * 1.4426950408889
 // maximum of the raw scores as the maximum of the scaled ones).
 bool scale_ok(float scale) { return scale > 0.f && __builtin_isfinite(scale); }
 
+long long round_up(long long x, long long q) { return (x + q - 1) / q * q; }
+
+// Split-KV prefill workspace: a 256-byte header holding the two chunk
+// counters, then max logits, exp-sums and normalized outputs, each section
+// 256-byte aligned.
+constexpr long long kWsHeader = 256;
+constexpr long long kWsAlign = 256;
+constexpr int kChunkTile = 32;       // key chunks are whole KV tiles
+constexpr int kChunkQuantum = 256;   // automatic chunk sizes are multiples of this
+constexpr int kMinChunk = 512;
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,6 +264,105 @@ int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.scale_log2 = log2e_scaled(scale);
     a.out = static_cast<uint16_t *>(out);
+    a.chunk = 0;
+    a.max_splits = 0;
+    a.ws_m = a.ws_l = a.ws_o = nullptr;
+    a.counters = nullptr;
+    a.stream = static_cast<hipStream_t>(stream);
+    return pa::launch_prefill(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
+                                  int max_blocks_per_seq, int block_size) {
+    if (num_seqs <= 0 || total_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        max_blocks_per_seq <= 0 || block_size <= 0 || num_q_heads % num_kv_heads != 0)
+        return 0;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > kMaxGroup) return 0;
+    const long long rows = pa::kPfRowSlots / group;
+    const long long pairs = ceil_div(total_q, rows) + num_seqs;
+    if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs) return 0;
+    const long long lmax = (long long)max_blocks_per_seq * block_size;
+    // about eight chunks per CU if every pair had the longest context
+    const long long target = 8LL * device_cu_count();
+    long long chunk = ceil_div(pairs * num_kv_heads * lmax, target);
+    chunk = ceil_div(chunk, kChunkQuantum) * kChunkQuantum;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    if (chunk > pa::kPfMaxChunk) chunk = pa::kPfMaxChunk;
+    return chunk >= lmax ? 0 : (int)chunk;
+}
+
+long long paged_attn_prefill_workspace_size(int total_q, int num_q_heads, int head_dim,
+                                            int max_blocks_per_seq, int block_size, int kv_chunk) {
+    if (total_q < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+        block_size <= 0 || kv_chunk <= 0)
+        return -1;
+    const long long splits = ceil_div((long long)max_blocks_per_seq * block_size, kv_chunk);
+    const long long recs = (long long)total_q * num_q_heads * splits;
+    return kWsHeader + 2 * round_up(recs * 4, kWsAlign) + round_up(recs * head_dim * 4, kWsAlign);
+}
+
+int paged_attn_prefill_ragged_split(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *seq_lens,
+                                    const int32_t *cu_seqlens, int num_seqs, int total_q,
+                                    int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, int max_blocks_per_seq,
+                                    float scale, int kv_chunk, void *workspace,
+                                    long long workspace_bytes, void *out, void *stream) {
+    int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
+    if (st != PA_OK) return st;
+    if (!cu_seqlens || !out) return PA_ERR_NULL_POINTER;
+    if (!scale_ok(scale)) return PA_ERR_BAD_VALUE;
+    if (total_q < 0 || max_q_len < 0) return PA_ERR_BAD_SHAPE;
+    if (!aligned16(out)) return PA_ERR_ALIGNMENT;
+    if (kv_chunk < 0 || kv_chunk % kChunkTile != 0 || kv_chunk > pa::kPfMaxChunk) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+    if (max_q_len > total_q) return PA_ERR_BAD_SHAPE;
+    int chunk = kv_chunk;
+    if (chunk == 0)
+        chunk = paged_attn_prefill_chunk_size(num_seqs, total_q, num_q_heads, num_kv_heads,
+                                              max_blocks_per_seq, block_size);
+    const int group = num_q_heads / num_kv_heads;
+    const long long pairs = ceil_div(total_q, pa::kPfRowSlots / group) + num_seqs;
+    if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs) chunk = 0;  // single pass
+    if (chunk > 0 && chunk >= (long long)max_blocks_per_seq * block_size) chunk = 0;
+    pa::PrefillArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_cache = static_cast<const uint16_t *>(k_cache);
+    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.cu_seqlens = cu_seqlens;
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale_log2 = log2e_scaled(scale);
+    a.out = static_cast<uint16_t *>(out);
+    a.chunk = 0;
+    a.max_splits = 0;
+    a.ws_m = a.ws_l = a.ws_o = nullptr;
+    a.counters = nullptr;
+    if (chunk > 0) {
+        if (!workspace) return PA_ERR_NULL_POINTER;
+        if (!aligned16(workspace)) return PA_ERR_ALIGNMENT;
+        const long long need = paged_attn_prefill_workspace_size(total_q, num_q_heads, head_dim,
+                                                                 max_blocks_per_seq, block_size, chunk);
+        if (need < 0 || workspace_bytes < need) return PA_ERR_BAD_SHAPE;
+        const long long splits = ceil_div((long long)max_blocks_per_seq * block_size, chunk);
+        const long long recs = (long long)total_q * num_q_heads * splits;
+        char *w = static_cast<char *>(workspace);
+        a.chunk = chunk;
+        a.max_splits = (int)splits;
+        a.counters = reinterpret_cast<int32_t *>(w);
+        a.ws_m = reinterpret_cast<float *>(w + kWsHeader);
+        a.ws_l = reinterpret_cast<float *>(w + kWsHeader + round_up(recs * 4, kWsAlign));
+        a.ws_o = reinterpret_cast<float *>(w + kWsHeader + 2 * round_up(recs * 4, kWsAlign));
+    }
     a.stream = static_cast<hipStream_t>(stream);
     return pa::launch_prefill(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

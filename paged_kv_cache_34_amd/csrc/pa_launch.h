@@ -33,6 +33,12 @@ struct ReduceArgs {
     hipStream_t stream;
 };
 
+// Split-KV prefill limits: the chunk list is built in LDS.
+constexpr int kPfMaxSeqs = 1024;    // sequences
+constexpr int kPfMaxPairs = 1024;   // (sequence, query tile) pairs
+constexpr int kPfMaxChunk = 8192;   // key chunk, tokens
+constexpr int kPfRowSlots = 256;    // (row, head) query slots of a prefill workgroup
+
 struct PrefillArgs {
     const uint16_t *q;
     const uint16_t *k_cache;
@@ -44,6 +50,11 @@ struct PrefillArgs {
     int max_blocks_per_seq;
     float scale_log2;
     uint16_t *out;
+    // split-KV (chunk > 0): partial records [total_q, H_q, max_splits] (+ D for
+    // the outputs) and two int counters, zero on entry and left zero
+    int chunk, max_splits;
+    float *ws_m, *ws_l, *ws_o;
+    int32_t *counters;
     hipStream_t stream;
 };
 

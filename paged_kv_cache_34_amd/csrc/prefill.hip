@@ -25,6 +25,18 @@
 //     reads of 4 tokens per 32x16 operand);
 //   * online softmax per slot with a lazy running max (rescale only when a
 //     tile's max exceeds it by more than 2^8), fp32 accumulation.
+//
+// Two launch forms:
+//   * single pass: one workgroup per (query tile, kv head, sequence) walks all
+//     of its keys and writes bf16 rows;
+//   * split-KV: a (query tile, kv head) is cut into key chunks of C tokens
+//     (the BI-V100 page's partitioning, section 2 "Level 3", applied to the
+//     query tiles of a prefill).  A persistent grid takes the chunks from a
+//     device counter, full chunks first and then the remainder chunks longest
+//     first, so the long contexts no longer set the critical path.  Rows whose
+//     keys all fall in the first chunk are written directly; the other rows
+//     leave one partial record (running max, exp-sum, normalized output) per
+//     chunk, and a merge kernel combines them with the page's combine rule.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -35,12 +47,14 @@ namespace pa {
 namespace {
 constexpr int kPfWaves = 8;
 constexpr int kPfSlots = kPfWaves * 32;  // (row, head) query slots per workgroup
+static_assert(kPfSlots == kPfRowSlots, "slots per workgroup");
 constexpr int kKvTile = 32;              // KV tokens per tile
 constexpr int kPfDepth = 3;              // register tiles in flight ahead of the one consumed
 constexpr float kPfTau = 8.0f;
 constexpr int kPfIdsLds = 1024;          // block ids staged in LDS (covers 16,384 tokens)
 // Fourth word of a raw buffer descriptor on the GFX9 family (32-bit data, no swizzle).
 constexpr int kPfBufferFlags = 0x00020000;
+constexpr int kPfMaxBuckets = kPfMaxChunk / kKvTile + 1;  // remainder-length buckets (tiles)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2_pf __attribute__((ext_vector_type(2)));
@@ -56,17 +70,40 @@ __device__ __forceinline__ float sum_xor32_pf(float x) {
 }
 }  // namespace
 
+// Kernel argument block (validated on the host).
+struct PfParams {
+    const uint16_t *q, *k_cache, *v_cache;
+    const int32_t *block_tables, *seq_lens, *cu_seqlens;
+    int num_seqs, total_q, num_q_heads, num_kv_heads, max_blocks_per_seq;
+    float scale_log2;
+    uint16_t *out;
+    // split-KV only
+    int chunk, max_splits;  // key chunk C (multiple of the tile); partial slots per (row, head)
+    float *ws_m, *ws_l, *ws_o;
+    int *counters;          // [0] next chunk to take, [1] workgroups done
+};
+
+// LDS of the tile pipeline.
+template <int D>
+struct __attribute__((aligned(16))) PfLds {
+    uint16_t k[2][kKvTile * (D + 8)];   // K rows, +8 bf16 pad: conflict-free b128 reads
+    uint16_t v[2][kKvTile * (D + 32)];  // V rows, +32 bf16 pad: the 4 rows x 64 bytes a
+                                        // transposed read takes per 32 lanes hit all 64 banks
+    int ids[kPfIdsLds];
+};
+
+// Keys [key_begin, key_end) of query tile `qtile` of sequence `seq`, kv head
+// `kvh` (key_begin a multiple of the tile).  split < 0: the range is the
+// tile's whole causal range and every row is written as bf16.  split >= 0:
+// chunk `split` of size prm.chunk; rows whose keys all lie in the first chunk
+// are written as bf16 (by chunk 0), the others leave a partial record for
+// every chunk holding at least one of their keys.
 template <int D, int G>
-__global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_seqlens,
-    int num_q_heads, int num_kv_heads, int max_blocks_per_seq, float scale_log2,
-    uint16_t *__restrict__ out) {
+__device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds, int seq, int kvh,
+                                              int qtile, int key_begin, int key_end, int split) {
     constexpr int R = kPfSlots / G;        // query rows per workgroup
-    constexpr int KROW = D + 8;            // bf16 per staged K row (conflict-free b128 reads)
-    constexpr int VROW = D + 32;           // bf16 per staged V row: the 4 rows x 64 bytes a
-                                           // transposed read takes per 32 lanes hit all 64 banks
+    constexpr int KROW = D + 8;
+    constexpr int VROW = D + 32;
     constexpr int NK = D / 16;             // k-steps of S^T
     constexpr int ND = D / 32;             // 32-dim tiles of O^T
     constexpr int CPT = D / 8;             // 16-byte chunks per token row
@@ -74,20 +111,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     constexpr int PASSES = (kKvTile + TPP - 1) / TPP;
     constexpr int DEPTH = D >= 256 ? 1 : kPfDepth;
     static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKvTile * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKvTile * VROW];
-    __shared__ int ids_lds[kPfIdsLds];
+    const uint16_t *__restrict__ k_cache = prm.k_cache;
+    const uint16_t *__restrict__ v_cache = prm.v_cache;
+    const float scale_log2 = prm.scale_log2;
+    const int num_q_heads = prm.num_q_heads;
 
-    const int qtile = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
-    const int q0 = cu_seqlens[seq];
-    const int n = cu_seqlens[seq + 1] - q0;
+    const int q0 = prm.cu_seqlens[seq];
+    const int n = prm.cu_seqlens[seq + 1] - q0;
     const int r0 = qtile * R;
-    if (r0 >= n) return;
-    const int L = seq_lens[seq];
+    const int L = prm.seq_lens[seq];
     const int c = L - n;
     const int rows = min(R, n - r0);
-    const int kv_end = c + r0 + rows;  // keys [0, kv_end) are visible to some row
-    const int ntiles = (kv_end + kKvTile - 1) / kKvTile;
+    const int tb = key_begin / kKvTile;
+    const int te = (key_end + kKvTile - 1) / kKvTile;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -101,7 +137,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     u32x4 qf[NK];
     {
         const uint16_t *qrow =
-            q + ((long)(q0 + r0 + (q_ok ? rq : 0)) * num_q_heads + kvh * G + (q_ok ? hq : 0)) * D +
+            prm.q + ((long)(q0 + r0 + (q_ok ? rq : 0)) * num_q_heads + kvh * G + (q_ok ? hq : 0)) * D +
             grp * 8;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
@@ -117,19 +153,20 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int32_t *bt_row = block_tables + (long)seq * max_blocks_per_seq;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq;
     const long tile_elems = 16L * D;
-    const long blk_stride = (long)num_kv_heads * tile_elems;
+    const long blk_stride = (long)prm.num_kv_heads * tile_elems;
     const int ld_tok = tid / CPT, ld_chunk = tid % CPT;
-    // the block ids this workgroup walks, staged once (no table read in the loop)
-    const int nblk = (kv_end + 15) / 16;
-    for (int b = tid; b < min(nblk, kPfIdsLds); b += kPfWaves * 64) ids_lds[b] = bt_row[b];
+    // the block ids of the range, staged once (no table read in the loop)
+    const int b0 = key_begin / 16;
+    const int nblk = (key_end + 15) / 16 - b0;
+    for (int b = tid; b < min(nblk, kPfIdsLds); b += kPfWaves * 64) lds.ids[b] = bt_row[b0 + b];
     __syncthreads();
 
     // Tile tt's rows for this thread: one 16-byte chunk of token ps*TPP + ld_tok.
     // The 512/D tokens a wave loads in one pass lie in one 16-token block, so
     // the block id and the buffer descriptor are wave-uniform.  The descriptor
-    // covers only the block's rows below kv_end, so the rest of the last tile
+    // covers only the block's rows below key_end, so the rest of the last tile
     // and whole tiles past it read as zeros without touching memory, and the
     // loads stay unconditional.  Block ids come from LDS (staged above) or,
     // past the staged range, from the table with a scalar load.
@@ -141,9 +178,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         for (int ps = 0; ps < PASSES; ++ps) {
             const int tl0 = ps * TPP + wtok;   // the wave's first token within the tile
             const int b = (tt * kKvTile + tl0) >> 4;
-            const int rows = tl0 < kKvTile ? min(max(kv_end - b * 16, 0), 16) : 0;
+            const int rows = tl0 < kKvTile ? min(max(key_end - b * 16, 0), 16) : 0;
             int phys = 0;
-            if (rows > 0) phys = b < kPfIdsLds ? ids_lds[b] : bt_const[b];
+            if (rows > 0) phys = b - b0 < kPfIdsLds ? lds.ids[b - b0] : bt_const[b];
             phys = __builtin_amdgcn_readfirstlane(phys);
             const long base = (long)phys * blk_stride + kvh * tile_elems;
             const int bytes = rows * D * 2;
@@ -158,8 +195,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         for (int ps = 0; ps < PASSES; ++ps) {
             const int tl = ps * TPP + ld_tok;
             if (tl < kKvTile) {
-                *reinterpret_cast<u32x4 *>(&k_lds[buf][tl * KROW + ld_chunk * 8]) = kr[ps];
-                *reinterpret_cast<u32x4 *>(&v_lds[buf][tl * VROW + ld_chunk * 8]) = vr[ps];
+                *reinterpret_cast<u32x4 *>(&lds.k[buf][tl * KROW + ld_chunk * 8]) = kr[ps];
+                *reinterpret_cast<u32x4 *>(&lds.v[buf][tl * VROW + ld_chunk * 8]) = vr[ps];
             }
         }
     };
@@ -173,7 +210,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
         f32x16 s;
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
-        const uint16_t *kl = &k_lds[buf][col * KROW + grp * 8];
+        const uint16_t *kl = &lds.k[buf][col * KROW + grp * 8];
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             const u32x4 ka = *reinterpret_cast<const u32x4 *>(kl + kk * 16);
@@ -223,7 +260,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
             }
         }
         l_run += ls;
-        const uint16_t *vl = &v_lds[buf][0];
+        const uint16_t *vl = &lds.v[buf][0];
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
 #pragma unroll
@@ -246,8 +283,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     // software pipeline: ring of DEPTH+1 register tiles, double-buffered LDS
     u32x4 kreg[DEPTH + 1][PASSES], vreg[DEPTH + 1][PASSES];
 #pragma unroll
-    for (int d = 0; d <= DEPTH; ++d) load_regs(d, kreg[d], vreg[d]);
-    store_lds(0, kreg[0], vreg[0]);
+    for (int d = 0; d <= DEPTH; ++d) load_regs(tb + d, kreg[d], vreg[d]);
+    store_lds(tb & 1, kreg[0], vreg[0]);
     __syncthreads();
     // One step: compute tile tt from LDS; tile tt+1 (ring slot u+1) goes to
     // the other LDS buffer; slot u is refilled with tile tt + DEPTH + 1.
@@ -261,21 +298,24 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
     // Full groups of DEPTH + 1 steps have no guards, so the loop's back edge
     // always comes after the last slot's refill (the compiler's wait counts
     // for the ring stay exact); the remaining steps follow the loop.
-    int t0 = 0;
-    for (; t0 + DEPTH < ntiles; t0 += DEPTH + 1) {
+    int t0 = tb;
+    for (; t0 + DEPTH < te; t0 += DEPTH + 1) {
         step(t0, std::integral_constant<int, 0>{});
         if constexpr (DEPTH >= 1) step(t0 + 1, std::integral_constant<int, 1>{});
         if constexpr (DEPTH >= 2) step(t0 + 2, std::integral_constant<int, 2>{});
         if constexpr (DEPTH >= 3) step(t0 + 3, std::integral_constant<int, 3>{});
     }
-    if (t0 < ntiles) step(t0, std::integral_constant<int, 0>{});
-    if constexpr (DEPTH >= 2) if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
-    if constexpr (DEPTH >= 3) if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
+    if (t0 < te) step(t0, std::integral_constant<int, 0>{});
+    if constexpr (DEPTH >= 2) if (t0 + 1 < te) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (DEPTH >= 3) if (t0 + 2 < te) step(t0 + 2, std::integral_constant<int, 2>{});
 
     const float l_tot = sum_xor32_pf(l_run);
-    if (q_ok) {
+    if (!q_ok) return;
+    if (split >= 0 && limit < key_begin) return;  // no key of this row in the chunk
+    const int row = q0 + r0 + rq, head = kvh * G + hq;
+    if (split < 0 || limit < prm.chunk) {
         const float inv = 1.f / l_tot;
-        uint16_t *orow = out + ((long)(q0 + r0 + rq) * num_q_heads + kvh * G + hq) * D;
+        uint16_t *orow = prm.out + ((long)row * num_q_heads + head) * D;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -286,18 +326,271 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(
                 w[1] = pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
                 *reinterpret_cast<u32x2 *>(orow + d0) = w;
             }
+    } else {
+        const long rec = ((long)row * num_q_heads + head) * prm.max_splits + split;
+        if (grp == 0) {
+            prm.ws_m[rec] = m_run;
+            prm.ws_l[rec] = l_tot;
+        }
+        const float inv = 1.f / l_tot;
+        float *orec = prm.ws_o + rec * D;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = dt * 32 + i4 * 8 + 4 * grp;
+                *reinterpret_cast<f32x4 *>(orec + d0) =
+                    f32x4{o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv, o[dt][4 * i4 + 2] * inv,
+                          o[dt][4 * i4 + 3] * inv};
+            }
+    }
+}
+
+// Single pass: one workgroup per (query tile, kv head, sequence).
+template <int D, int G>
+__global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PfParams prm) {
+    constexpr int R = kPfSlots / G;
+    __shared__ PfLds<D> lds;
+    const int qtile = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+    const int q0 = prm.cu_seqlens[seq];
+    const int n = prm.cu_seqlens[seq + 1] - q0;
+    const int r0 = qtile * R;
+    if (r0 >= n) return;
+    const int c = prm.seq_lens[seq] - n;
+    const int kv_end = c + r0 + min(R, n - r0);  // keys [0, kv_end) are visible to some row
+    prefill_range<D, G>(prm, lds, seq, kvh, qtile, 0, kv_end, -1);
+}
+
+// Split-KV, persistent.  Every workgroup builds the same chunk list in LDS:
+//   pairs (sequence, query tile) in sequence order, with kv_end = the pair's
+//   last row's causal limit + 1;
+//   chunks: for every pair floor(kv_end / C) full chunks, then one remainder
+//   chunk if kv_end % C > 0; each chunk once per kv head.
+// Chunk order: all full chunks (pair, kv head, chunk), then the remainder
+// chunks by decreasing length (pair order among equals; a bitonic sort of the
+// pairs keeps it deterministic, so every workgroup sees the same list).
+// Workgroups take chunk indices from counters[0]; the last workgroup to
+// finish resets both counters to zero for the next launch.
+template <int D, int G>
+__global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfParams prm) {
+    constexpr int R = kPfSlots / G;
+    constexpr int T = kPfWaves * 64;
+    constexpr int SPT = (kPfMaxSeqs + T - 1) / T;   // sequences per thread
+    constexpr int PPT = (kPfMaxPairs + T - 1) / T;  // pairs per thread
+    static_assert(kPfMaxPairs == 2 * T, "one compare-exchange per thread and sort stage");
+    __shared__ PfLds<D> lds;
+    __shared__ int pr_seq[kPfMaxPairs], pr_qt[kPfMaxPairs], pr_kv[kPfMaxPairs];
+    __shared__ int fpref[kPfMaxPairs], rorder[kPfMaxPairs];
+    __shared__ int bcnt[kPfMaxBuckets];
+    __shared__ int wtot[kPfWaves], bcast[1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int S = prm.num_seqs, C = prm.chunk, hkv = prm.num_kv_heads;
+
+    // workgroup-wide exclusive scan of one value per thread
+    auto block_scan = [&](int v, int &total) {
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane == 63) wtot[wave] = incl;
+        __syncthreads();
+        int run = incl - v, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kPfWaves; ++w) {
+            if (w < wave) run += wtot[w];
+            tot += wtot[w];
+        }
+        __syncthreads();
+        total = tot;
+        return run;
+    };
+
+    // 1. pairs (sequence, query tile)
+    int nq[SPT];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int i = tid * SPT + k;
+        nq[k] = 0;
+        if (i < S) nq[k] = (prm.cu_seqlens[i + 1] - prm.cu_seqlens[i] + R - 1) / R;
+        local += nq[k];
+    }
+    int NP = 0;
+    int run = block_scan(local, NP);
+    NP = min(NP, kPfMaxPairs);
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int i = tid * SPT + k;
+        if (i < S) {
+            const int n = prm.cu_seqlens[i + 1] - prm.cu_seqlens[i];
+            const int c = prm.seq_lens[i] - n;
+            for (int qt = 0; qt < nq[k] && run + qt < kPfMaxPairs; ++qt) {
+                pr_seq[run + qt] = i;
+                pr_qt[run + qt] = qt;
+                pr_kv[run + qt] = c + qt * R + min(R, n - qt * R);
+            }
+        }
+        run += nq[k];
+    }
+    __syncthreads();
+
+    // 2. full chunks: prefix over pairs; remainders: sort keys
+    int fl[PPT];
+    int flocal = 0;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int p = tid * PPT + k;
+        fl[k] = p < NP ? (pr_kv[p] / C) * hkv : 0;
+        flocal += fl[k];
+        int key = 0x7fffffff;
+        if (p < NP) {
+            const int rem = pr_kv[p] % C;
+            if (rem > 0) key = ((kPfMaxBuckets - (rem + kKvTile - 1) / kKvTile) << 11) | p;
+        }
+        rorder[p] = key;
+    }
+    int F = 0;
+    int frun = block_scan(flocal, F);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int p = tid * PPT + k;
+        fpref[p] = frun;
+        frun += fl[k];
+    }
+    // bitonic sort of the keys, ascending (longest remainder first, then pair)
+    for (int k = 2; k <= kPfMaxPairs; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int i = 2 * tid - (tid & (j - 1));
+            const int l = i + j;
+            const int a = rorder[i], b = rorder[l];
+            if ((a > b) == ((i & k) == 0)) {
+                rorder[i] = b;
+                rorder[l] = a;
+            }
+            __syncthreads();
+        }
+    }
+    int nrem_local = 0;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) nrem_local += rorder[tid * PPT + k] != 0x7fffffff;
+    int NR = 0;
+    block_scan(nrem_local, NR);
+    const int total = F + NR * hkv;
+
+    // 3. take chunks
+    for (;;) {
+        if (tid == 0) bcast[0] = atomicAdd(prm.counters, 1);
+        __syncthreads();
+        const int it = __builtin_amdgcn_readfirstlane(bcast[0]);
+        if (it >= total) break;
+        int p, kvh, split;
+        if (it < F) {
+            int lo = 0, hi = NP;  // the last pair with fpref[p] <= it
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (fpref[mid] <= it) lo = mid; else hi = mid;
+            }
+            p = __builtin_amdgcn_readfirstlane(lo);
+            const int nf = __builtin_amdgcn_readfirstlane(pr_kv[p] / C);
+            const int r = it - fpref[p];
+            kvh = r / nf;
+            split = r % nf;
+        } else {
+            const int r = it - F;
+            p = rorder[r / hkv] & 2047;
+            kvh = r % hkv;
+            split = pr_kv[p] / C;
+        }
+        p = __builtin_amdgcn_readfirstlane(p);
+        kvh = __builtin_amdgcn_readfirstlane(kvh);
+        split = __builtin_amdgcn_readfirstlane(split);
+        const int kv_end = __builtin_amdgcn_readfirstlane(pr_kv[p]);
+        const int kb = split * C;
+        prefill_range<D, G>(prm, lds, __builtin_amdgcn_readfirstlane(pr_seq[p]), kvh,
+                            __builtin_amdgcn_readfirstlane(pr_qt[p]), kb, min(kb + C, kv_end), split);
+    }
+    if (tid == 0) {
+        const int done = __hip_atomic_fetch_add(prm.counters + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (int)gridDim.x - 1) {
+            __hip_atomic_store(prm.counters, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(prm.counters + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Merge of the split-KV partial records (the BI-V100 page's combine rule):
+// one workgroup per query row; rows whose keys all lie in the first chunk
+// were written by the prefill kernel and are skipped.
+template <int D>
+__global__ __launch_bounds__(256) void paged_prefill_merge_kernel(PfParams prm) {
+    const int row = blockIdx.x;
+    int lo = 0, hi = prm.num_seqs;  // the sequence owning the row: last s with cu[s] <= row
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (prm.cu_seqlens[mid] <= row) lo = mid; else hi = mid;
+    }
+    const int q0 = prm.cu_seqlens[lo];
+    const int n = prm.cu_seqlens[lo + 1] - q0;
+    const int visible = prm.seq_lens[lo] - n + (row - q0) + 1;
+    const int ns = (visible + prm.chunk - 1) / prm.chunk;
+    if (ns <= 1) return;
+    const int hq = prm.num_q_heads;
+    for (int e = threadIdx.x; e < hq * D; e += 256) {
+        const int h = e / D, d = e % D;
+        const long rec0 = ((long)row * hq + h) * prm.max_splits;
+        float M = -INFINITY;
+        for (int j = 0; j < ns; ++j) M = fmaxf(M, prm.ws_m[rec0 + j]);
+        float wsum = 0.f, acc = 0.f;
+        for (int j = 0; j < ns; ++j) {
+            const float w = fast_exp2(prm.ws_m[rec0 + j] - M) * prm.ws_l[rec0 + j];
+            wsum += w;
+            acc = fmaf(w, prm.ws_o[(rec0 + j) * D + d], acc);
+        }
+        prm.out[((long)row * hq + h) * D + d] = (uint16_t)f32_to_bf16_bits(acc / wsum);
     }
 }
 
 namespace {
+int pf_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int D, int G>
 hipError_t launch_prefill_dg(const PrefillArgs &a) {
     constexpr int R = kPfSlots / G;
-    dim3 grid((a.max_q_len + R - 1) / R, a.num_kv_heads, a.num_seqs);
+    PfParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.cu_seqlens,
+                 a.num_seqs, a.total_q, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
+                 a.scale_log2, a.out, a.chunk, a.max_splits, a.ws_m, a.ws_l, a.ws_o, a.counters};
     dim3 block(kPfWaves * 64);
-    hipLaunchKernelGGL((paged_prefill_kernel<D, G>), grid, block, 0, a.stream, a.q, a.k_cache,
-                       a.v_cache, a.block_tables, a.seq_lens, a.cu_seqlens, a.num_q_heads,
-                       a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2, a.out);
+    if (a.chunk > 0) {
+        static int per_cu = 0;  // resident workgroups per CU for this instantiation
+        if (per_cu == 0) {
+            int nb = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_prefill_split_kernel<D, G>,
+                                                             block.x, 0) != hipSuccess || nb <= 0)
+                nb = 1;
+            per_cu = nb;
+        }
+        hipLaunchKernelGGL((paged_prefill_split_kernel<D, G>), dim3(pf_cu_count() * per_cu), block, 0,
+                           a.stream, prm);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.total_q), dim3(256), 0, a.stream, prm);
+        return hipGetLastError();
+    }
+    dim3 grid((a.max_q_len + R - 1) / R, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((paged_prefill_kernel<D, G>), grid, block, 0, a.stream, prm);
     return hipGetLastError();
 }
 

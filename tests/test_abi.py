@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol(lib):
     names = pa.declared_functions()
     assert set(names) == {
         "paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
-        "paged_attn_prefill_ragged",
+        "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
+        "paged_attn_prefill_chunk_size", "paged_attn_prefill_workspace_size",
         "paged_attn_num_partitions", "paged_attn_choose_partition_size",
         "paged_attn_prefill_tile_map", "paged_attn_status_string"} | (
         set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
@@ -182,3 +183,68 @@ def test_fused_decode_validation(lib, over, status):
                                      a["P"], a["out"], a["ml"], a["es"], a["to"], a["NP"], a["cnt"],
                                      None)
     assert st == status
+
+
+def split_call(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, S=2, total_q=300, max_q=200, Hq=32,
+             Hkv=8, D=128, bs=16, nb=1024, mbps=500, scale=0.125, chunk=256, ws=FAKE,
+             wsb=1 << 40, out=FAKE)
+    a.update(over)
+    return lib.paged_attn_prefill_ragged_split(
+        a["q"], a["k"], a["v"], a["bt"], a["sl"], a["cu"], a["S"], a["total_q"], a["max_q"], a["Hq"],
+        a["Hkv"], a["D"], a["bs"], a["nb"], a["mbps"], a["scale"], a["chunk"], a["ws"], a["wsb"],
+        a["out"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cu=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(out=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(ws=NULL, S=0), pa.PA_OK),
+    (dict(scale=0.0), pa.PA_ERR_BAD_VALUE),
+    (dict(chunk=-32), pa.PA_ERR_BAD_SHAPE),
+    (dict(chunk=48), pa.PA_ERR_BAD_SHAPE),
+    (dict(chunk=8192 + 32), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 2), pa.PA_ERR_ALIGNMENT),
+    (dict(max_q=301), pa.PA_ERR_BAD_SHAPE),
+    (dict(S=0), pa.PA_OK),
+    (dict(total_q=0, max_q=0), pa.PA_OK),
+])
+def test_prefill_split_validation(lib, over, status):
+    assert split_call(lib, **over) == status
+
+
+def test_prefill_split_workspace_checks(lib):
+    # a chunk that splits needs a workspace of the documented size
+    need = pa.paged_attn_prefill_workspace_size(300, 32, 128, 500, 16, 256)
+    assert split_call(lib, ws=NULL) == pa.PA_ERR_NULL_POINTER
+    assert split_call(lib, ws=FAKE + 8) == pa.PA_ERR_ALIGNMENT
+    assert split_call(lib, wsb=need - 1) == pa.PA_ERR_BAD_SHAPE
+
+
+def test_prefill_workspace_size_formula(lib):
+    def ru(x):
+        return (x + 255) // 256 * 256
+    for total_q, hq, d, mbps, chunk in [(300, 32, 128, 500, 256), (1, 1, 64, 1, 32),
+                                        (1815, 32, 128, 525, 1536), (7, 12, 256, 100, 8192)]:
+        splits = -(-mbps * 16 // chunk)
+        recs = total_q * hq * splits
+        assert pa.paged_attn_prefill_workspace_size(total_q, hq, d, mbps, 16, chunk) == \
+            256 + 2 * ru(recs * 4) + ru(recs * d * 4)
+    assert pa.paged_attn_prefill_workspace_size(10, 4, 64, 10, 16, 0) == -1
+    assert pa.paged_attn_prefill_workspace_size(10, 0, 64, 10, 16, 64) == -1
+
+
+def test_prefill_chunk_size_heuristic(lib):
+    # Without a GPU the device has 256 CUs in this formula: chunk =
+    # ceil((ceil(total_q / (256 / G)) + S) * H_kv * L_max / (8 * 256)), rounded up
+    # to 256, clamped to [512, 8192]; 0 when it covers L_max or the pairs overflow.
+    # ragged prefill shape: 16 sequences, 1815 rows, G = 4, L_max = 525 * 16
+    assert pa.paged_attn_prefill_chunk_size(16, 1815, 32, 8, 525, 16) == 1536
+    # one sequence, 64 new rows after a 100k context: many chunks for 8 workgroups
+    assert pa.paged_attn_prefill_chunk_size(1, 64, 32, 8, 6250, 16) == 1024
+    # short contexts: one chunk would cover them, so single pass
+    assert pa.paged_attn_prefill_chunk_size(4, 100, 32, 8, 8, 16) == 0
+    # more than 1024 (sequence, query tile) pairs: single pass
+    assert pa.paged_attn_prefill_chunk_size(2000, 4000, 32, 8, 100, 16) == 0
+    assert pa.paged_attn_prefill_chunk_size(0, 10, 32, 8, 100, 16) == 0

@@ -16,21 +16,43 @@ def orc():
     return oracle.get()
 
 
-def run_prefill(dev):
+# Launch forms every parity case runs in: the single pass, the split-KV form
+# with its automatic chunk, and the split-KV form with 64-token chunks (many
+# chunks per row, remainders of every length, multi-chunk merges).
+MODES = ("single", "split-auto", "split-64")
+
+
+def workspace_for(dev, chunk):
+    c = dev.case
+    return pa.PrefillWorkspace(c.num_seqs, c.total_q, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                               c.max_blocks_per_seq, 16, "cuda", kv_chunk=chunk)
+
+
+def run_prefill(dev, mode="single", ws=None):
     t = torch()
     c = dev.case
     out = t.full_like(dev.q, float("nan"))
-    pa.paged_attn_prefill_ragged(dev.q, dev.k, dev.v, dev.bt, dev.sl, dev.cu, c.max_q_len,
-                                 float(c.scale), out)
+    if mode == "single":
+        pa.paged_attn_prefill_ragged(dev.q, dev.k, dev.v, dev.bt, dev.sl, dev.cu, c.max_q_len,
+                                     float(c.scale), out)
+    else:
+        chunk = 0 if mode == "split-auto" else int(mode.split("-")[1])
+        if ws is None:
+            ws = workspace_for(dev, chunk)
+        pa.paged_attn_prefill_ragged_split(dev.q, dev.k, dev.v, dev.bt, dev.sl, dev.cu, c.max_q_len,
+                                           float(c.scale), out, workspace=ws.buffer, kv_chunk=chunk)
     t.cuda.synchronize()
     return out
 
 
 def check(orc, case, what):
-    announce(f"{what}: prefill S={case.num_seqs} total_q={case.total_q} Hq={case.num_q_heads} "
-             f"Hkv={case.num_kv_heads} D={case.head_dim}")
-    got = bf16_host_f64(run_prefill(Dev(case)))
-    assert_out_close(got, orc.prefill_case(case), what)
+    ref = orc.prefill_case(case)
+    dev = Dev(case)
+    for mode in MODES:
+        announce(f"{what} [{mode}]: prefill S={case.num_seqs} total_q={case.total_q} "
+                 f"Hq={case.num_q_heads} Hkv={case.num_kv_heads} D={case.head_dim}")
+        got = bf16_host_f64(run_prefill(dev, mode))
+        assert_out_close(got, ref, f"{what} [{mode}]")
 
 
 def test_ragged_prefill_config(orc):
@@ -62,11 +84,13 @@ def test_group_sizes_not_dividing_slots(orc, G):
 
 def test_single_row_sequences_match_oracle_decode(orc):
     case = workloads.prefill_case("onerow", 700, [1] * 6, [0, 1, 15, 16, 1000, 4095], 32, 8, 128)
-    announce("one row per sequence")
-    got = bf16_host_f64(run_prefill(Dev(case)))
     ref = orc.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
                      case.num_kv_heads, case.scale)
-    assert_out_close(got, ref, "one-row prefill vs decode oracle")
+    dev = Dev(case)
+    for mode in MODES:
+        announce(f"one row per sequence [{mode}]")
+        got = bf16_host_f64(run_prefill(dev, mode))
+        assert_out_close(got, ref, f"one-row prefill vs decode oracle [{mode}]")
 
 
 def test_empty_sequences_in_batch(orc):
@@ -83,8 +107,40 @@ def test_block_shuffle_is_bit_identical():
     case2 = workloads.PagedCase(**{**case.__dict__, "k_cache": case.k_cache[inv],
                                    "v_cache": case.v_cache[inv],
                                    "block_tables": perm[case.block_tables].astype(np.int32)})
-    announce("prefill shuffle invariance + determinism")
-    a = bf16_bits_host(run_prefill(Dev(case)))
-    b = bf16_bits_host(run_prefill(Dev(case2)))
-    c = bf16_bits_host(run_prefill(Dev(case)))
-    assert np.array_equal(a, b) and np.array_equal(a, c)
+    d1, d2 = Dev(case), Dev(case2)
+    for mode in MODES:
+        announce(f"prefill shuffle invariance + determinism [{mode}]")
+        a = bf16_bits_host(run_prefill(d1, mode))
+        b = bf16_bits_host(run_prefill(d2, mode))
+        c = bf16_bits_host(run_prefill(d1, mode))
+        assert np.array_equal(a, b) and np.array_equal(a, c), mode
+
+
+def test_split_long_context_and_counters(orc):
+    """Contexts of several thousand tokens cut into many chunks; the workspace
+    counters are zero again after every call, and repeated calls sharing one
+    workspace give the same bits."""
+    case = workloads.prefill_case("plong", 704, [200, 3, 64, 129], [6000, 7000, 0, 2500], 32, 8, 128)
+    ref = orc.prefill_case(case)
+    dev = Dev(case)
+    for chunk in (0, 256, 2048):
+        ws = workspace_for(dev, chunk)
+        announce(f"long contexts, chunk {chunk} (auto={ws.kv_chunk})")
+        first = run_prefill(dev, "split-auto" if chunk == 0 else f"split-{chunk}", ws)
+        assert_out_close(bf16_host_f64(first), ref, f"long contexts chunk {chunk}")
+        assert int(ws.buffer[:8].view(torch().int32).abs().sum().item()) == 0
+        again = run_prefill(dev, "split-auto" if chunk == 0 else f"split-{chunk}", ws)
+        assert np.array_equal(bf16_bits_host(first), bf16_bits_host(again))
+        assert int(ws.buffer[:8].view(torch().int32).abs().sum().item()) == 0
+
+
+def test_split_falls_back_to_single_pass_without_workspace(orc):
+    case = workloads.prefill_case("pfall", 705, [20, 9], [30, 0], 8, 2, 64)
+    dev = Dev(case)
+    announce("split form with one chunk covering every context")
+    out = torch().full_like(dev.q, float("nan"))
+    pa.paged_attn_prefill_ragged_split(dev.q, dev.k, dev.v, dev.bt, dev.sl, dev.cu,
+                                       case.max_q_len, float(case.scale), out, workspace=None,
+                                       kv_chunk=8192)
+    torch().cuda.synchronize()
+    assert_out_close(bf16_host_f64(out), orc.prefill_case(case), "split fallback")
