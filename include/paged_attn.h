@@ -147,7 +147,7 @@ int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_
  * leave one fp32 partial record (running max, exp-sum, normalized output) per
  * chunk, merged by a second kernel with the page's combine rule.
  *   kv_chunk   0 = paged_attn_prefill_chunk_size(...); else a positive
- *              multiple of 32, at most 8192.
+ *              multiple of 64, at most 8192.
  *   workspace  device memory, 16-byte aligned, of at least
  *              paged_attn_prefill_workspace_size(...) bytes for the chunk in
  *              use.  Its first 8 bytes are two counters that must be zero
@@ -155,7 +155,8 @@ int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_
  *              allocation); every completed call leaves them zero.  Calls
  *              that overlap in time must not share a workspace.
  * When the chunk list does not fit (more than 1024 sequences or (sequence,
- * query tile) pairs) or one chunk covers the longest context, the call runs
+ * query tile) pairs, or more than 128 query heads) or one chunk covers the
+ * longest context, the call runs
  * the single-pass kernel and does not touch the workspace (it may then be
  * NULL).  Same status codes as paged_attn_prefill_ragged, plus
  * PA_ERR_BAD_SHAPE for a bad kv_chunk or a workspace that is too small.
@@ -173,7 +174,8 @@ int paged_attn_prefill_ragged_split(const void *q, const void *k_cache, const vo
 /* Key chunk the split-KV prefill uses when kv_chunk == 0: about eight chunks
  * per CU of the current device if every (sequence, query tile) pair had the
  * longest context, a multiple of 256 in [512, 8192]; 0 when the single pass
- * is used instead (too many pairs, or one chunk covers the longest context).
+ * is used instead (too many pairs or query heads, or one chunk covers the
+ * longest context).
  * The pair count is bounded by ceil(total_q / (256 / G)) + num_seqs. */
 int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
                                   int max_blocks_per_seq, int block_size);

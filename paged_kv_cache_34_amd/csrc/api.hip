@@ -50,7 +50,7 @@ long long round_up(long long x, long long q) { return (x + q - 1) / q * q; }
 // 256-byte aligned.
 constexpr long long kWsHeader = 256;
 constexpr long long kWsAlign = 256;
-constexpr int kChunkTile = 32;       // key chunks are whole KV tiles
+constexpr int kChunkTile = 64;       // key chunks are whole KV tiles (64 keys for D <= 128)
 constexpr int kChunkQuantum = 256;   // automatic chunk sizes are multiples of this
 constexpr int kMinChunk = 512;
 
@@ -281,7 +281,7 @@ int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, in
     if (group > kMaxGroup) return 0;
     const long long rows = pa::kPfRowSlots / group;
     const long long pairs = ceil_div(total_q, rows) + num_seqs;
-    if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs) return 0;
+    if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs || num_q_heads > pa::kPfMaxHeads) return 0;
     const long long lmax = (long long)max_blocks_per_seq * block_size;
     // about eight chunks per CU if every pair had the longest context
     const long long target = 8LL * device_cu_count();
@@ -325,7 +325,8 @@ int paged_attn_prefill_ragged_split(const void *q, const void *k_cache, const vo
                                               max_blocks_per_seq, block_size);
     const int group = num_q_heads / num_kv_heads;
     const long long pairs = ceil_div(total_q, pa::kPfRowSlots / group) + num_seqs;
-    if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs) chunk = 0;  // single pass
+    if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs || num_q_heads > pa::kPfMaxHeads)
+        chunk = 0;  // single pass
     if (chunk > 0 && chunk >= (long long)max_blocks_per_seq * block_size) chunk = 0;
     pa::PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);

@@ -38,6 +38,7 @@ constexpr int kPfMaxSeqs = 1024;    // sequences
 constexpr int kPfMaxPairs = 1024;   // (sequence, query tile) pairs
 constexpr int kPfMaxChunk = 8192;   // key chunk, tokens
 constexpr int kPfRowSlots = 256;    // (row, head) query slots of a prefill workgroup
+constexpr int kPfMaxHeads = 128;    // query heads (the merge keeps a row's chunk weights in LDS)
 
 struct PrefillArgs {
     const uint16_t *q;

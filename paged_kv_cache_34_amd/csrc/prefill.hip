@@ -48,13 +48,15 @@ namespace {
 constexpr int kPfWaves = 8;
 constexpr int kPfSlots = kPfWaves * 32;  // (row, head) query slots per workgroup
 static_assert(kPfSlots == kPfRowSlots, "slots per workgroup");
-constexpr int kKvTile = 32;              // KV tokens per tile
-constexpr int kPfDepth = 3;              // register tiles in flight ahead of the one consumed
+// KV tokens per tile: 64 (two S accumulators per wave) where the LDS allows
+template <int D> constexpr int pf_tile() { return D >= 256 ? 32 : 64; }
+constexpr int kTileMin = 32;
+constexpr int kPfDepth = 2;              // register tiles in flight ahead of the one consumed
 constexpr float kPfTau = 8.0f;
 constexpr int kPfIdsLds = 1024;          // block ids staged in LDS (covers 16,384 tokens)
 // Fourth word of a raw buffer descriptor on the GFX9 family (32-bit data, no swizzle).
 constexpr int kPfBufferFlags = 0x00020000;
-constexpr int kPfMaxBuckets = kPfMaxChunk / kKvTile + 1;  // remainder-length buckets (tiles)
+constexpr int kPfMaxBuckets = kPfMaxChunk / kTileMin + 1;  // remainder-length buckets (32 keys)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2_pf __attribute__((ext_vector_type(2)));
@@ -86,8 +88,8 @@ struct PfParams {
 // LDS of the tile pipeline.
 template <int D>
 struct __attribute__((aligned(16))) PfLds {
-    uint16_t k[2][kKvTile * (D + 8)];   // K rows, +8 bf16 pad: conflict-free b128 reads
-    uint16_t v[2][kKvTile * (D + 32)];  // V rows, +32 bf16 pad: the 4 rows x 64 bytes a
+    uint16_t k[2][pf_tile<D>() * (D + 8)];   // K rows, +8 bf16 pad: conflict-free b128 reads
+    uint16_t v[2][pf_tile<D>() * (D + 32)];  // V rows, +32 bf16 pad: the 4 rows x 64 bytes a
                                         // transposed read takes per 32 lanes hit all 64 banks
     int ids[kPfIdsLds];
 };
@@ -108,7 +110,9 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
     constexpr int ND = D / 32;             // 32-dim tiles of O^T
     constexpr int CPT = D / 8;             // 16-byte chunks per token row
     constexpr int TPP = kPfWaves * 64 / CPT;  // tokens loaded per pass
-    constexpr int PASSES = (kKvTile + TPP - 1) / TPP;
+    constexpr int KT = pf_tile<D>();       // keys per tile
+    constexpr int NSA = KT / 32;           // S^T accumulators (32 keys each) per tile
+    constexpr int PASSES = (KT + TPP - 1) / TPP;
     constexpr int DEPTH = D >= 256 ? 1 : kPfDepth;
     static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
     const uint16_t *__restrict__ k_cache = prm.k_cache;
@@ -122,8 +126,8 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
     const int L = prm.seq_lens[seq];
     const int c = L - n;
     const int rows = min(R, n - r0);
-    const int tb = key_begin / kKvTile;
-    const int te = (key_end + kKvTile - 1) / kKvTile;
+    const int tb = key_begin / KT;
+    const int te = (key_end + KT - 1) / KT;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,8 +181,8 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int tl0 = ps * TPP + wtok;   // the wave's first token within the tile
-            const int b = (tt * kKvTile + tl0) >> 4;
-            const int rows = tl0 < kKvTile ? min(max(key_end - b * 16, 0), 16) : 0;
+            const int b = (tt * KT + tl0) >> 4;
+            const int rows = tl0 < KT ? min(max(key_end - b * 16, 0), 16) : 0;
             int phys = 0;
             if (rows > 0) phys = b - b0 < kPfIdsLds ? lds.ids[b - b0] : bt_const[b];
             phys = __builtin_amdgcn_readfirstlane(phys);
@@ -194,7 +198,7 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int tl = ps * TPP + ld_tok;
-            if (tl < kKvTile) {
+            if (tl < KT) {
                 *reinterpret_cast<u32x4 *>(&lds.k[buf][tl * KROW + ld_chunk * 8]) = kr[ps];
                 *reinterpret_cast<u32x4 *>(&lds.v[buf][tl * VROW + ld_chunk * 8]) = vr[ps];
             }
@@ -207,33 +211,44 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
     const int vt_col = 16 * (gamma & 1) + 4 * (rho & 3);              // + 32 dt
 
     auto compute = [&](int tt, int buf) {
-        f32x16 s;
+        // S^T of the tile's NSA blocks of 32 keys: independent accumulator
+        // chains, interleaved
+        f32x16 s[NSA];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+        for (int a = 0; a < NSA; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[a][i] = 0.f;
         const uint16_t *kl = &lds.k[buf][col * KROW + grp * 8];
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-            const u32x4 ka = *reinterpret_cast<const u32x4 *>(kl + kk * 16);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
-                                                        __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
-        }
-        // lane holds tokens (i/4)*8 + 4*grp + i%4 of this tile for query slot `col`;
-        // only tiles reaching past the first row's causal limit (or the end
-        // of the visible keys) need the mask.  With scale > 0 the max of the
-        // raw scores gives the max of the scaled ones, and the scaling folds
-        // into the exponent's FMA below.
-        const int tbase = tt * kKvTile + 4 * grp;
-        float mr = -INFINITY;
-        if (tt * kKvTile + kKvTile - 1 > c + r0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = tbase + (i >> 2) * 8 + (i & 3);
-                s[i] = (t <= limit) ? s[i] : -INFINITY;
-                mr = fmaxf(mr, s[i]);
+            for (int a = 0; a < NSA; ++a) {
+                const u32x4 ka = *reinterpret_cast<const u32x4 *>(kl + a * 32 * KROW + kk * 16);
+                s[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
+                                                               __builtin_bit_cast(bf16x8, qf[kk]), s[a], 0, 0, 0);
             }
+        }
+        // lane holds tokens 32a + (i/4)*8 + 4*grp + i%4 of this tile for query
+        // slot `col`; only tiles reaching past the first row's causal limit
+        // (or the end of the visible keys) need the mask.  With scale > 0 the
+        // max of the raw scores gives the max of the scaled ones, and the
+        // scaling folds into the exponent's FMA below.
+        const int tbase = tt * KT + 4 * grp;
+        float mr = -INFINITY;
+        if (tt * KT + KT - 1 > c + r0) {
+#pragma unroll
+            for (int a = 0; a < NSA; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = tbase + 32 * a + (i >> 2) * 8 + (i & 3);
+                    s[a][i] = (t <= limit) ? s[a][i] : -INFINITY;
+                    mr = fmaxf(mr, s[a][i]);
+                }
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[i]);
+            for (int a = 0; a < NSA; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[a][i]);
         }
         const float bm = max_xor32_pf(mr) * scale_log2;  // tile max, log2 units
         if (__any(bm > m_run + kPfTau)) {
@@ -247,24 +262,27 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
         // a slot that has seen no visible key yet keeps m_run = -inf; its
         // probabilities are zero (exp2(-inf) after shifting by a finite 0)
         const float msh = (m_run == -INFINITY) ? 0.f : m_run;
-        u32x4 pk[2];
+        u32x4 pk[2 * NSA];
         float ls = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int a = 0; a < NSA; ++a)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float a = fast_exp2(fmaf(s[8 * h + 2 * k], scale_log2, -msh));
-                const float b = fast_exp2(fmaf(s[8 * h + 2 * k + 1], scale_log2, -msh));
-                ls += a + b;
-                pk[h][k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_pf{a, b}, bf16x2_pf));
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float x0 = fast_exp2(fmaf(s[a][8 * h + 2 * k], scale_log2, -msh));
+                    const float x1 = fast_exp2(fmaf(s[a][8 * h + 2 * k + 1], scale_log2, -msh));
+                    ls += x0 + x1;
+                    pk[2 * a + h][k] =
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_pf{x0, x1}, bf16x2_pf));
+                }
             }
-        }
         l_run += ls;
         const uint16_t *vl = &lds.v[buf][0];
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
+        for (int ks = 0; ks < 2 * NSA; ++ks) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int dt = 0; dt < ND; ++dt) {
                 // A operand: V[16 ks + 8 h + 4 (lane/32) + 0..3][dim lane%32 + 32 dt], h = 0, 1
                 const uint16_t *a0 = vl + (16 * ks + vt_row) * VROW + 32 * dt + vt_col;
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -448,7 +466,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
         int key = 0x7fffffff;
         if (p < NP) {
             const int rem = pr_kv[p] % C;
-            if (rem > 0) key = ((kPfMaxBuckets - (rem + kKvTile - 1) / kKvTile) << 11) | p;
+            if (rem > 0) key = ((kPfMaxBuckets - (rem + kTileMin - 1) / kTileMin) << 11) | p;
         }
         rorder[p] = key;
     }
@@ -523,9 +541,17 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
 
 // Merge of the split-KV partial records (the BI-V100 page's combine rule):
 // one workgroup per query row; rows whose keys all lie in the first chunk
-// were written by the prefill kernel and are skipped.
+// were written by the prefill kernel and are skipped.  The chunk weights
+// w_j = 2^(m_j - M) l_j / sum_j' 2^(m_j' - M) l_j' of every head go to LDS
+// first; then each thread forms 4 consecutive output dims of one head from
+// 16-byte loads of the chunk outputs, chunks in a fixed order.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxHeads = kPfMaxHeads;  // query heads per row held in LDS
+constexpr int kMergeMaxSplits = 64;   // chunks per row held in LDS (more: a second pass)
+
 template <int D>
-__global__ __launch_bounds__(256) void paged_prefill_merge_kernel(PfParams prm) {
+__global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfParams prm) {
+    __shared__ float wts[kMergeMaxHeads * kMergeMaxSplits];
     const int row = blockIdx.x;
     int lo = 0, hi = prm.num_seqs;  // the sequence owning the row: last s with cu[s] <= row
     while (hi - lo > 1) {
@@ -538,18 +564,56 @@ __global__ __launch_bounds__(256) void paged_prefill_merge_kernel(PfParams prm) 
     const int ns = (visible + prm.chunk - 1) / prm.chunk;
     if (ns <= 1) return;
     const int hq = prm.num_q_heads;
-    for (int e = threadIdx.x; e < hq * D; e += 256) {
-        const int h = e / D, d = e % D;
-        const long rec0 = ((long)row * hq + h) * prm.max_splits;
-        float M = -INFINITY;
-        for (int j = 0; j < ns; ++j) M = fmaxf(M, prm.ws_m[rec0 + j]);
-        float wsum = 0.f, acc = 0.f;
-        for (int j = 0; j < ns; ++j) {
-            const float w = fast_exp2(prm.ws_m[rec0 + j] - M) * prm.ws_l[rec0 + j];
-            wsum += w;
-            acc = fmaf(w, prm.ws_o[(rec0 + j) * D + d], acc);
+    const long rec_row = (long)row * hq * prm.max_splits;
+    for (int j0 = 0; j0 < ns; j0 += kMergeMaxSplits) {
+        // weights of chunks j0 .. j0+nj-1 relative to the max and sum over all ns
+        const int nj = min(kMergeMaxSplits, ns - j0);
+        for (int h = threadIdx.x; h < hq; h += kMergeThreads) {
+            const float *mh = prm.ws_m + rec_row + (long)h * prm.max_splits;
+            const float *lh = prm.ws_l + rec_row + (long)h * prm.max_splits;
+            float M = -INFINITY;
+            for (int j = 0; j < ns; ++j) M = fmaxf(M, mh[j]);
+            float wsum = 0.f;
+            for (int j = 0; j < ns; ++j) wsum += fast_exp2(mh[j] - M) * lh[j];
+            const float inv = 1.f / wsum;
+            for (int j = 0; j < nj; ++j) wts[h * kMergeMaxSplits + j] = fast_exp2(mh[j0 + j] - M) * lh[j0 + j] * inv;
         }
-        prm.out[((long)row * hq + h) * D + d] = (uint16_t)f32_to_bf16_bits(acc / wsum);
+        __syncthreads();
+        for (int e = threadIdx.x; e < hq * (D / 4); e += kMergeThreads) {
+            const int h = e / (D / 4), d0 = (e % (D / 4)) * 4;
+            const float *w = wts + h * kMergeMaxSplits;
+            const float *o = prm.ws_o + (rec_row + (long)h * prm.max_splits + j0) * D + d0;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (j0 > 0) {  // continue the first pass's sum, kept in the output tile
+                const float *prev = reinterpret_cast<const float *>(prm.ws_o) +
+                                    (rec_row + (long)h * prm.max_splits) * D + d0;
+                acc = *reinterpret_cast<const f32x4 *>(prev);
+            }
+            int j = 0;
+            for (; j + 4 <= nj; j += 4) {
+                const f32x4 a0 = *reinterpret_cast<const f32x4 *>(o + (long)(j + 0) * D);
+                const f32x4 a1 = *reinterpret_cast<const f32x4 *>(o + (long)(j + 1) * D);
+                const f32x4 a2 = *reinterpret_cast<const f32x4 *>(o + (long)(j + 2) * D);
+                const f32x4 a3 = *reinterpret_cast<const f32x4 *>(o + (long)(j + 3) * D);
+                acc += w[j] * a0;
+                acc += w[j + 1] * a1;
+                acc += w[j + 2] * a2;
+                acc += w[j + 3] * a3;
+            }
+            for (; j < nj; ++j) acc += w[j] * *reinterpret_cast<const f32x4 *>(o + (long)j * D);
+            if (j0 + nj < ns) {
+                // more chunks follow: park the running sum in chunk 0's record
+                float *first = prm.ws_o + (rec_row + (long)h * prm.max_splits) * D + d0;
+                *reinterpret_cast<f32x4 *>(first) = acc;
+            } else {
+                uint16_t *orow = prm.out + ((long)row * hq + h) * D + d0;
+                u32x2 wv;
+                wv[0] = pack_bf16x2(acc[0], acc[1]);
+                wv[1] = pack_bf16x2(acc[2], acc[3]);
+                *reinterpret_cast<u32x2 *>(orow) = wv;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -586,7 +650,7 @@ hipError_t launch_prefill_dg(const PrefillArgs &a) {
                            a.stream, prm);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.total_q), dim3(256), 0, a.stream, prm);
+        hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.total_q), dim3(kMergeThreads), 0, a.stream, prm);
         return hipGetLastError();
     }
     dim3 grid((a.max_q_len + R - 1) / R, a.num_kv_heads, a.num_seqs);

@@ -203,7 +203,8 @@ def split_call(lib, **over):
     (dict(scale=0.0), pa.PA_ERR_BAD_VALUE),
     (dict(chunk=-32), pa.PA_ERR_BAD_SHAPE),
     (dict(chunk=48), pa.PA_ERR_BAD_SHAPE),
-    (dict(chunk=8192 + 32), pa.PA_ERR_BAD_SHAPE),
+    (dict(chunk=96), pa.PA_ERR_BAD_SHAPE),
+    (dict(chunk=8192 + 64), pa.PA_ERR_BAD_SHAPE),
     (dict(D=96), pa.PA_ERR_UNSUPPORTED),
     (dict(out=FAKE + 2), pa.PA_ERR_ALIGNMENT),
     (dict(max_q=301), pa.PA_ERR_BAD_SHAPE),
@@ -248,3 +249,5 @@ def test_prefill_chunk_size_heuristic(lib):
     # more than 1024 (sequence, query tile) pairs: single pass
     assert pa.paged_attn_prefill_chunk_size(2000, 4000, 32, 8, 100, 16) == 0
     assert pa.paged_attn_prefill_chunk_size(0, 10, 32, 8, 100, 16) == 0
+    # more than 128 query heads: single pass
+    assert pa.paged_attn_prefill_chunk_size(2, 100, 256, 16, 1000, 16) == 0
