@@ -427,25 +427,78 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         }
         __syncthreads();
         if (flag[0]) {
-            for (int e = tid; e < G * D; e += NW * 64) {
-                const int h = e / D, d = e % D;
+            // The merge runs over (column, slot) pairs: a column is 4
+            // consecutive dims of one head; a column's SL slots take the
+            // partitions round-robin, 4 at a time with every load issued
+            // before any is used, each slot keeping a running max; then the
+            // slots are folded in LDS in slot order (deterministic).
+            constexpr int T = NW * 64;
+            constexpr int COLS = G * D / 4;
+            constexpr int SL = T / COLS >= 1 ? T / COLS : 1;
+            constexpr int MU = 4;
+            float *fold = lds;  // [SL][COLS][6]: max, weight sum, 4 accumulators
+            static_assert(SL * COLS * 6 <= S::MAIN_FLOATS, "merge fold fits the scratch");
+            for (int pr = tid; pr < COLS * SL; pr += T) {
+                const int c = pr % COLS, sl = pr / COLS;
+                const int h = c / (D / 4), d0 = 4 * (c % (D / 4));
                 float *mlr = prm.max_logits + (row0 + h) * max_num_partitions;
                 float *esr = prm.exp_sums + (row0 + h) * max_num_partitions;
-                float *tor = prm.tmp_out + (row0 + h) * max_num_partitions * (long)D + d;
-                float m = -INFINITY, wsum = 0.f, acc = 0.f;
-                for (int p = 0; p < nparts; ++p) {
-                    const float mp = load_partial(mlr + p);
-                    if (mp > m) {
-                        const float f = fast_exp2((m - mp) * kLog2e);
-                        acc *= f;
-                        wsum *= f;
-                        m = mp;
+                float *tor = prm.tmp_out + (row0 + h) * max_num_partitions * (long)D + d0;
+                float m = -INFINITY, wsum = 0.f;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int p0 = sl; p0 < nparts; p0 += SL * MU) {
+                    float mp[MU], lp[MU], op[MU][4];
+#pragma unroll
+                    for (int u = 0; u < MU; ++u) {
+                        const int p = p0 + u * SL;
+                        const bool ok = p < nparts;
+                        mp[u] = ok ? load_partial(mlr + p) : -INFINITY;
+                        lp[u] = ok ? load_partial(esr + p) : 0.f;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) op[u][k] = ok ? load_partial(tor + (long)p * D + k) : 0.f;
                     }
-                    const float w = fast_exp2((mp - m) * kLog2e) * load_partial(esr + p);
-                    acc = fmaf(w, load_partial(tor + (long)p * D), acc);
-                    wsum += w;
+#pragma unroll
+                    for (int u = 0; u < MU; ++u) {
+                        if (p0 + u * SL >= nparts) continue;
+                        if (mp[u] > m) {
+                            const float f = fast_exp2((m - mp[u]) * kLog2e);
+                            wsum *= f;
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) acc[k] *= f;
+                            m = mp[u];
+                        }
+                        const float w = fast_exp2((mp[u] - m) * kLog2e) * lp[u];
+                        wsum += w;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, op[u][k], acc[k]);
+                    }
                 }
-                prm.out[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(acc / wsum);
+                float *f6 = fold + (sl * COLS + c) * 6;
+                f6[0] = m;
+                f6[1] = wsum;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) f6[2 + k] = acc[k];
+            }
+            __syncthreads();
+            for (int c = tid; c < COLS; c += T) {
+                const int h = c / (D / 4), d0 = 4 * (c % (D / 4));
+                float M = -INFINITY;
+#pragma unroll
+                for (int sl = 0; sl < SL; ++sl) M = fmaxf(M, fold[(sl * COLS + c) * 6]);
+                float ws = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < SL; ++sl) {
+                    const float *f6 = fold + (sl * COLS + c) * 6;
+                    const float f = f6[1] > 0.f ? fast_exp2((f6[0] - M) * kLog2e) : 0.f;
+                    ws = fmaf(f, f6[1], ws);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) a[k] = fmaf(f, f6[2 + k], a[k]);
+                }
+                const float inv = 1.f / ws;
+                u32x2 wv;
+                wv[0] = pack_bf16x2(a[0] * inv, a[1] * inv);
+                wv[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
+                *reinterpret_cast<u32x2 *>(prm.out + (row0 + h) * D + d0) = wv;
             }
             if (tid == 0)
                 __hip_atomic_store(prm.counters + (long)seq * prm.num_kv_heads + kvh, 0, __ATOMIC_RELAXED,
@@ -594,22 +647,34 @@ __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
     const float *esr = exp_sums + row * max_num_partitions;
     const int slot = tid / LPP, dl = tid % LPP;
     const float *base = tmp_out + row * (long)max_num_partitions * head_dim + chunk * kReduceChunk + dl * 4;
-    // The first round of partition records is loaded before the sequence
-    // length is known (records past the sequence's partitions are discarded
-    // by selection, never used in arithmetic), which takes one dependent
-    // memory round trip off the kernel.
+    // When the partial buffers hold at most one record per slot, the first
+    // round is loaded before the sequence length is known (records past the
+    // sequence's partitions are discarded by selection, never used in
+    // arithmetic), which takes one dependent memory round trip off the
+    // kernel.  With more partition slots than that, most of them are unused
+    // for short sequences, so the length comes first and only existing
+    // partitions are read.
+    const bool speculate = max_num_partitions <= SLOTS;
+    int n = 0;
+    if (!speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    const int first_bound = speculate ? max_num_partitions : n;
     float mv[kReduceUnroll], ev[kReduceUnroll];
     f32x4 v[kReduceUnroll];
 #pragma unroll
     for (int u = 0; u < kReduceUnroll; ++u) {
         const int p = slot + u * SLOTS;
-        const bool in = p < max_num_partitions;
+        const bool in = p < first_bound;
         mv[u] = in ? mlr[p] : -INFINITY;
         ev[u] = in ? esr[p] : 0.f;
         v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int L = seq_lens[seq];
-    const int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    if (speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
     uint16_t *o = out + row * head_dim + chunk * kReduceChunk;
     if (n == 0) {
         for (int d = tid; d < kReduceChunk; d += NW * 64) o[d] = 0;
@@ -664,6 +729,109 @@ __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
             ws = fmaf(f, sw[sl], ws);
         }
         o[d] = (uint16_t)f32_to_bf16_bits(a / ws);
+    }
+}
+
+// Cross-partition merge for partial buffers with few partition slots (a
+// batch of many sequences with a handful of partitions each): one wave per
+// (sequence, query head).  The wave's lanes form R = 256 / D rows of D / 4
+// lanes (4 dims per lane); the rows take partitions round-robin, 4 at a time
+// with every load issued before any is used, each row keeping a running max.
+// The rows are then folded with lane swaps (rows 16 and 32 lanes apart) using
+// only symmetric operations, so every lane of a fold holds the same result.
+// When every slot fits in the first round, the records are loaded before the
+// sequence length is known (records past the sequence's partitions are
+// discarded by selection, never used in arithmetic).
+constexpr int kWaveReduceUnroll = 4;
+constexpr int kWaveReduceMaxRounds = 8;  // slots per row beyond this use paged_reduce_kernel
+
+template <int D>
+__global__ __launch_bounds__(256) void paged_reduce_wave_kernel(
+    const float *__restrict__ max_logits, const float *__restrict__ exp_sums,
+    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens, int num_seqs,
+    int num_q_heads, int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
+    constexpr int LPR = D / 4;   // lanes per row
+    constexpr int R = 64 / LPR;  // rows per wave
+    constexpr int U = kWaveReduceUnroll;
+    const int lane = threadIdx.x & 63;
+    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // sequence * H_q + head
+    if (pair >= (long)num_seqs * num_q_heads) return;
+    const int seq = (int)(pair / num_q_heads);
+    const int r = lane / LPR, d0 = 4 * (lane % LPR);
+    const float *mlr = max_logits + pair * max_num_partitions;
+    const float *esr = exp_sums + pair * max_num_partitions;
+    const float *base = tmp_out + pair * (long)max_num_partitions * D + d0;
+    const bool speculate = max_num_partitions <= R * U;
+    int n = 0;
+    if (!speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    const int first_bound = speculate ? max_num_partitions : n;
+    float mv[U], ev[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int p = r + u * R;
+        const bool in = p < first_bound;
+        mv[u] = in ? mlr[p] : -INFINITY;
+        ev[u] = in ? esr[p] : 0.f;
+        v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    uint16_t *o = out + pair * D + d0;
+    if (n == 0) {
+        if (r == 0) *reinterpret_cast<u32x2 *>(o) = u32x2{0u, 0u};
+        return;
+    }
+    float m = -INFINITY, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = r;; p0 += R * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (p0 + u * R >= n) continue;
+            if (mv[u] > m) {  // rescale what was accumulated to the new max
+                const float f = fast_exp2((m - mv[u]) * kLog2e);
+                acc *= f;
+                wsum *= f;
+                m = mv[u];
+            }
+            const float w = fast_exp2((mv[u] - m) * kLog2e) * ev[u];
+            acc[0] = fmaf(w, v[u][0], acc[0]);
+            acc[1] = fmaf(w, v[u][1], acc[1]);
+            acc[2] = fmaf(w, v[u][2], acc[2]);
+            acc[3] = fmaf(w, v[u][3], acc[3]);
+            wsum += w;
+        }
+        const int q0 = p0 + R * U;
+        if (__all(q0 >= n)) break;  // wave-uniform exit; rows past n load nothing below
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = q0 + u * R;
+            const bool ok = p < n;
+            mv[u] = ok ? mlr[p] : -INFINITY;
+            ev[u] = ok ? esr[p] : 0.f;
+            v[u] = ok ? *reinterpret_cast<const f32x4 *>(base + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // fold the rows: rescale each to the common max, then sum
+    auto fold = [&](auto max_x, auto sum_x) {
+        const float M = max_x(m);
+        const float f = wsum > 0.f ? fast_exp2((m - M) * kLog2e) : 0.f;
+        wsum = sum_x(f * wsum);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = sum_x(f * acc[k]);
+        m = M;
+    };
+    if constexpr (R >= 4) fold([](float x) { return max_xor16(x); }, [](float x) { return sum_xor16(x); });
+    if constexpr (R >= 2) fold([](float x) { return max_xor32(x); }, [](float x) { return sum_xor32(x); });
+    if (r == 0) {
+        const float inv = 1.f / wsum;
+        *reinterpret_cast<u32x2 *>(o) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                             pack_bf16x2(acc[2] * inv, acc[3] * inv)};
     }
 }
 
@@ -766,6 +934,17 @@ hipError_t launch_decode(const DecodeArgs &a) {
 }
 
 hipError_t launch_reduce(const ReduceArgs &a) {
+    const int rows = 256 / a.head_dim;  // rows of the one-wave merge
+    if (a.max_num_partitions <= rows * kWaveReduceUnroll * kWaveReduceMaxRounds) {
+        const long pairs = (long)a.num_seqs * a.num_q_heads;
+        dim3 grid((unsigned)((pairs + 3) / 4));
+        auto kern = a.head_dim == 64 ? paged_reduce_wave_kernel<64>
+                  : a.head_dim == 128 ? paged_reduce_wave_kernel<128> : paged_reduce_wave_kernel<256>;
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, a.max_logits, a.exp_sums, a.tmp_out,
+                           a.seq_lens, a.num_seqs, a.num_q_heads, a.partition_size, a.max_num_partitions,
+                           a.out);
+        return hipGetLastError();
+    }
     dim3 grid(a.head_dim / kReduceChunk, a.num_q_heads, a.num_seqs);
     dim3 block(kReduceWaves * 64);
     hipLaunchKernelGGL((paged_reduce_kernel<kReduceWaves>), grid, block, 0, a.stream, a.max_logits,

@@ -139,17 +139,32 @@ def test_repeat_runs_are_bitwise_equal():
     assert np.array_equal(bf16_bits_host(a[3]), bf16_bits_host(b[3]))
 
 
-def test_reduce_on_oracle_partials(orc):
-    """The merge kernel alone, fed fp32-rounded oracle partials."""
+# (head_dim, partition size, lengths, which merge kernel the partition count selects)
+REDUCE_CASES = [
+    (256, 256, [1, 100, 2000, 5000], "one wave per (sequence, head), length read first"),
+    (256, 64, [1, 100, 2000, 5000], "workgroup per (64 dims, head, sequence)"),
+    (128, 512, [1, 100, 2000, 3000], "one wave, records loaded before the length"),
+    (64, 16, [1, 100, 700, 2000], "one wave, eight rounds"),
+    (64, 16, [1, 100, 700, 2100], "workgroup per (64 dims, head, sequence)"),
+]
+
+
+@pytest.mark.parametrize("D,P,lens,kind", REDUCE_CASES)
+def test_reduce_on_oracle_partials(orc, D, P, lens, kind):
+    """The merge kernels alone, fed fp32-rounded oracle partials; the slots of
+    partitions that do not exist hold NaN and must never reach the output."""
     t = torch()
-    case = workloads.build_case("reduce", 305, [1, 100, 2000, 5000], 12, 2, 256)
-    P = 256
+    case = workloads.build_case("reduce", 305, lens, 12, 2, D)
     ml, es, to = orc.partials_case(case, P)
     ml32, es32, to32 = (np.nan_to_num(x).astype(np.float32) for x in (ml, es, to))
     ref = orc.reduce(ml32.astype(np.float64), es32.astype(np.float64), to32.astype(np.float64),
                      case.seq_lens, P)
+    for s, L in enumerate(case.seq_lens):
+        n = (int(L) + P - 1) // P
+        for a in (ml32, es32, to32):
+            a[s, :, n:] = np.nan
     out = t.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=t.bfloat16, device="cuda")
-    announce("reduce kernel alone")
+    announce(f"reduce kernel alone: D={D} P={P} slots={ml32.shape[2]} ({kind})")
     pa.paged_attn_decode_reduce(t.from_numpy(ml32).cuda(), t.from_numpy(es32).cuda(),
                                 t.from_numpy(to32).cuda(), t.from_numpy(case.seq_lens).cuda(), P, out)
     t.cuda.synchronize()
@@ -237,7 +252,8 @@ def run_fused(dev, P, ws=None):
 
 
 @pytest.mark.parametrize("name,P", [("tiny", 16), ("tiny", 48), ("edges", 512), ("edges", 256),
-                                    ("llama3", 512), ("ragged", 1024), ("many", 64)])
+                                    ("llama3", 512), ("ragged", 1024), ("many", 64), ("long", 512),
+                                    ("g16d256", 128), ("g1d64", 16)])
 def test_fused_merge(orc, name, P):
     if name == "tiny":
         case = workloads.tiny_decode()
@@ -247,6 +263,12 @@ def test_fused_merge(orc, name, P):
         case = workloads.llama3_8b_decode()
     elif name == "ragged":
         case = workloads.large_ragged_decode()
+    elif name == "long":
+        case = workloads.long_split_decode()
+    elif name == "g16d256":  # more (head, 4-dim) merge columns than threads
+        case = workloads.build_case("fused_g16", 322, EDGE_LENS, 16, 1, 256)
+    elif name == "g1d64":    # many merge slots per column
+        case = workloads.build_case("fused_g1", 323, EDGE_LENS, 2, 2, 64)
     else:
         rng = np.random.default_rng(321)
         case = workloads.build_case("fused_many", 321, rng.integers(1, 400, size=1100), 8, 2, 64)
