@@ -18,6 +18,13 @@ Definitions followed (details in the C source):
   prefill     -- AstrAI page, "Q Scheduling and KV Addressing" (qo_indptr rows),
                  causal rule of the RL.cu page's prefill kernel, end-aligned.
   tile_map    -- AstrAI page, "Q Scheduling and KV Addressing" worked example.
+  kv_append   -- the cache write before decode/prefill (AstrAI page, backend
+                 layer: it "owns KV cache writes and reads"); new rows are the
+                 last rows of each sequence, placed like the prefill rows.
+  fp8         -- FP8 (OCP E4M3) KV cache with a per-position dequant scale (B200
+                 page, "Stage D: FP8 Paged KV Gather" and "FP8 KV
+                 Quantize/Dequant"): quantize_fp8, fp8_dequant, kv_append_fp8,
+                 and decode / partials over the dequantized (fp64) cache.
 """
 from __future__ import annotations
 
@@ -66,8 +73,23 @@ class Oracle:
         lib.oracle_reduce.argtypes = [_f64p, _f64p, _f64p, _i32p] + [_c_int] * 5 + [_f64p]
         lib.oracle_prefill.argtypes = [_u16p, _u16p, _u16p, _i32p, _i32p, _i32p] + [_c_int] * 7 + [
             ctypes.c_float, _f64p]
+        _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+        _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+        lib.oracle_decode_f64kv.argtypes = [_u16p, _f64p, _f64p, _i32p, _i32p] + [_c_int] * 6 + [
+            ctypes.c_float, _f64p]
+        lib.oracle_decode_partials_f64kv.argtypes = [_u16p, _f64p, _f64p, _i32p, _i32p] + [_c_int] * 6 + [
+            ctypes.c_float, _c_int, _c_int, _f64p, _f64p, _f64p]
+        lib.oracle_kv_append.argtypes = [_u16p, _u16p, _i32p, _i32p, _i32p] + [_c_int] * 5 + [_u16p, _u16p]
+        lib.oracle_kv_append_fp8.argtypes = ([_u16p, _u16p, _i32p, _i32p, _i32p] + [_c_int] * 5 +
+                                             [_u8p, _u8p, _f32p, _f32p])
+        lib.oracle_quantize_fp8.argtypes = [_u16p, ctypes.c_long, _c_int, _u8p, _f32p]
+        lib.oracle_fp8_dequant.argtypes = [_u8p, _f32p, ctypes.c_long, _c_int, _f64p]
+        lib.oracle_e4m3_value.argtypes = [_c_int]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
         for fn in ("oracle_decode", "oracle_decode_partials", "oracle_reduce", "oracle_prefill",
-                   "oracle_mutant", "oracle_num_threads"):
+                   "oracle_mutant", "oracle_num_threads", "oracle_decode_f64kv",
+                   "oracle_decode_partials_f64kv", "oracle_kv_append", "oracle_kv_append_fp8",
+                   "oracle_quantize_fp8", "oracle_fp8_dequant"):
             getattr(lib, fn).restype = ctypes.c_int
         self.lib = lib
 
@@ -151,6 +173,112 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_prefill rejected the shapes (status {rc})")
         return out
+
+    # ---- O1 / O2 over fp64 caches (dequantized FP8) ----------------------
+    def decode_f64kv(self, q, k_values, v_values, block_tables, seq_lens, num_kv_heads: int,
+                     scale) -> np.ndarray:
+        q = self._c(q, np.uint16)
+        S, Hq, D = q.shape
+        kc = self._c(k_values, np.float64)
+        bt = self._c(block_tables, np.int32)
+        out = np.empty((S, Hq, D), dtype=np.float64)
+        rc = self.lib.oracle_decode_f64kv(q, kc, self._c(v_values, np.float64), bt,
+                                          self._c(seq_lens, np.int32), S, Hq, num_kv_heads, D,
+                                          kc.shape[2], bt.shape[1], float(np.float32(scale)), out)
+        if rc:
+            raise ValueError(f"oracle_decode_f64kv rejected the shapes (status {rc})")
+        return out
+
+    def decode_partials_f64kv(self, q, k_values, v_values, block_tables, seq_lens,
+                              num_kv_heads: int, scale, partition_size: int,
+                              max_num_partitions: Optional[int] = None):
+        q = self._c(q, np.uint16)
+        S, Hq, D = q.shape
+        kc = self._c(k_values, np.float64)
+        bs = kc.shape[2]
+        bt = self._c(block_tables, np.int32)
+        if max_num_partitions is None:
+            max_num_partitions = max(1, (bt.shape[1] * bs + partition_size - 1) // partition_size)
+        NP = int(max_num_partitions)
+        ml = np.full((S, Hq, NP), np.nan)
+        es = np.full((S, Hq, NP), np.nan)
+        to = np.full((S, Hq, NP, D), np.nan)
+        rc = self.lib.oracle_decode_partials_f64kv(q, kc, self._c(v_values, np.float64), bt,
+                                                   self._c(seq_lens, np.int32), S, Hq, num_kv_heads,
+                                                   D, bs, bt.shape[1], float(np.float32(scale)),
+                                                   int(partition_size), NP, ml, es, to)
+        if rc:
+            raise ValueError(f"oracle_decode_partials_f64kv rejected the shapes (status {rc})")
+        return ml, es, to
+
+    # ---- KV append ---------------------------------------------------------
+    def kv_append(self, k_new, v_new, block_tables, seq_lens, cu_seqlens, k_cache, v_cache):
+        """Copies of the bf16 caches with the new rows written; inputs untouched."""
+        kn = self._c(k_new, np.uint16)
+        kc = np.array(k_cache, dtype=np.uint16, copy=True, order="C")
+        vc = np.array(v_cache, dtype=np.uint16, copy=True, order="C")
+        bt = self._c(block_tables, np.int32)
+        sl = self._c(seq_lens, np.int32)
+        _, Hkv, bs, D = kc.shape
+        rc = self.lib.oracle_kv_append(kn, self._c(v_new, np.uint16), bt, sl,
+                                       self._c(cu_seqlens, np.int32), sl.shape[0], Hkv, D, bs,
+                                       bt.shape[1], kc, vc)
+        if rc:
+            raise ValueError(f"oracle_kv_append rejected the inputs (status {rc})")
+        return kc, vc
+
+    # ---- FP8 ---------------------------------------------------------------
+    def e4m3_value(self, code: int) -> float:
+        return float(self.lib.oracle_e4m3_value(int(code)))
+
+    def quantize_fp8(self, x_bits):
+        """Rows of bf16 bits [..., D] -> (E4M3 codes uint8 [..., D], scales float32 [...])."""
+        x = self._c(x_bits, np.uint16)
+        D = x.shape[-1]
+        rows = x.size // D if D else 0
+        codes = np.empty(x.shape, dtype=np.uint8)
+        scales = np.empty(x.shape[:-1], dtype=np.float32)
+        self.lib.oracle_quantize_fp8(x, rows, D, codes, scales)
+        return codes, scales
+
+    def fp8_dequant(self, codes, scales) -> np.ndarray:
+        c = self._c(codes, np.uint8)
+        sc = self._c(scales, np.float32)
+        D = c.shape[-1]
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_fp8_dequant(c, sc, c.size // D if D else 0, D, out)
+        return out
+
+    def kv_append_fp8(self, k_new, v_new, block_tables, seq_lens, cu_seqlens, k_codes, v_codes,
+                      k_scales, v_scales):
+        """Copies of the FP8 caches (codes, scales) with the new rows quantized and written."""
+        kc = np.array(k_codes, dtype=np.uint8, copy=True, order="C")
+        vc = np.array(v_codes, dtype=np.uint8, copy=True, order="C")
+        ks = np.array(k_scales, dtype=np.float32, copy=True, order="C")
+        vs = np.array(v_scales, dtype=np.float32, copy=True, order="C")
+        bt = self._c(block_tables, np.int32)
+        sl = self._c(seq_lens, np.int32)
+        _, Hkv, bs, D = kc.shape
+        rc = self.lib.oracle_kv_append_fp8(self._c(k_new, np.uint16), self._c(v_new, np.uint16), bt,
+                                           sl, self._c(cu_seqlens, np.int32), sl.shape[0], Hkv, D,
+                                           bs, bt.shape[1], kc, vc, ks, vs)
+        if rc:
+            raise ValueError(f"oracle_kv_append_fp8 rejected the inputs (status {rc})")
+        return kc, vc, ks, vs
+
+    def decode_fp8(self, q, k_codes, v_codes, k_scales, v_scales, block_tables, seq_lens,
+                   num_kv_heads: int, scale) -> np.ndarray:
+        return self.decode_f64kv(q, self.fp8_dequant(k_codes, k_scales),
+                                 self.fp8_dequant(v_codes, v_scales), block_tables, seq_lens,
+                                 num_kv_heads, scale)
+
+    def decode_partials_fp8(self, q, k_codes, v_codes, k_scales, v_scales, block_tables, seq_lens,
+                            num_kv_heads: int, scale, partition_size: int,
+                            max_num_partitions: Optional[int] = None):
+        return self.decode_partials_f64kv(q, self.fp8_dequant(k_codes, k_scales),
+                                          self.fp8_dequant(v_codes, v_scales), block_tables,
+                                          seq_lens, num_kv_heads, scale, partition_size,
+                                          max_num_partitions)
 
     # ---- case conveniences ----------------------------------------------
     def decode_case(self, case) -> np.ndarray:

@@ -63,19 +63,28 @@ static int kv_head_of(int h, int Hq, int Hkv) {
 #endif
 }
 
-/* Address of token t's row of kv head g for sequence s: the logical block
- * t / bs is looked up in the block table, the slot is t % bs (RL.cu page,
+/* A KV cache as the oracle reads it, [num_blocks, H_kv, block_size, D]:
+ * bf16 bit patterns, or fp64 values (a dequantized FP8 cache). */
+typedef struct {
+    const uint16_t *bf16;
+    const double *f64;
+} kv_cache_t;
+
+static double kv_elem(kv_cache_t c, long i) { return c.bf16 ? bf16_to_double(c.bf16[i]) : c.f64[i]; }
+
+/* Element offset of token t's row of kv head g for sequence s: the logical
+ * block t / bs is looked up in the block table, the slot is t % bs (RL.cu page,
  * paged decode kernel: "logical block index -> physical block in the pool";
  * cache layout [num_blocks, H_kv, block_size, D]). */
-static const uint16_t *kv_row(const uint16_t *cache, const int32_t *block_tables,
-                              int s, int t, int g, int Hkv, int bs, int D, int mbps) {
+static long kv_row(const int32_t *block_tables, int s, int t, int g, int Hkv, int bs, int D,
+                   int mbps) {
     long phys = block_tables[(long)s * mbps + t / bs];
 #if ORACLE_MUTANT == 4
     int slot = (t + 1) % bs;
 #else
     int slot = t % bs;
 #endif
-    return cache + (((phys * Hkv + g) * (long)bs + slot) * (long)D);
+    return ((phys * Hkv + g) * (long)bs + slot) * (long)D;
 }
 
 static const uint16_t *q_row(const uint16_t *q, long row, int h, int Hq, int D, long rows) {
@@ -90,9 +99,9 @@ static const uint16_t *q_row(const uint16_t *q, long row, int h, int Hq, int D, 
 
 /* Scaled score z_t = scale * q . k_t (BI-V100 design page, section 1
  * "Problem Definition": softmax(Q[h] K[t]^T / sqrt(d)) V[t]). */
-static double score(const uint16_t *qr, const uint16_t *kr, int D, double scale) {
+static double score(const uint16_t *qr, kv_cache_t k, long kr, int D, double scale) {
     double acc = 0.0;
-    for (int d = 0; d < D; ++d) acc += bf16_to_double(qr[d]) * bf16_to_double(kr[d]);
+    for (int d = 0; d < D; ++d) acc += bf16_to_double(qr[d]) * kv_elem(k, kr + d);
 #if ORACLE_MUTANT == 1
     (void)scale;
     return acc;
@@ -104,7 +113,7 @@ static double score(const uint16_t *qr, const uint16_t *kr, int D, double scale)
 /* softmax over keys [t0, t1) of sequence s, weighted sum of values:
  * m = max z, l = sum exp(z - m), out = sum exp(z - m) v / l.
  * Returns m and l through the pointers (used by the partial routine). */
-static void attend_range(const uint16_t *qr, const uint16_t *k_cache, const uint16_t *v_cache,
+static void attend_range(const uint16_t *qr, kv_cache_t k_cache, kv_cache_t v_cache,
                          const int32_t *block_tables, int s, int g, int t0, int t1,
                          int Hkv, int bs, int D, int mbps, double scale,
                          double *z, double *out, double *m_out, double *l_out) {
@@ -114,8 +123,7 @@ static void attend_range(const uint16_t *qr, const uint16_t *k_cache, const uint
     int n = t1 - t0;
     double m = -INFINITY;
     for (int i = 0; i < n; ++i) {
-        const uint16_t *kr = kv_row(k_cache, block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
-        z[i] = score(qr, kr, D, scale);
+        z[i] = score(qr, k_cache, kv_row(block_tables, s, t0 + i, g, Hkv, bs, D, mbps), D, scale);
         if (z[i] > m) m = z[i];
     }
     double l = 0.0;
@@ -133,12 +141,12 @@ static void attend_range(const uint16_t *qr, const uint16_t *k_cache, const uint
     }
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     for (int i = 0; i < n; ++i) {
+        const long vr = kv_row(block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
 #if ORACLE_MUTANT == 6
-        const uint16_t *vr = kv_row(k_cache, block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
+        for (int d = 0; d < D; ++d) out[d] += z[i] * kv_elem(k_cache, vr + d);
 #else
-        const uint16_t *vr = kv_row(v_cache, block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
+        for (int d = 0; d < D; ++d) out[d] += z[i] * kv_elem(v_cache, vr + d);
 #endif
-        for (int d = 0; d < D; ++d) out[d] += z[i] * bf16_to_double(vr[d]);
     }
     for (int d = 0; d < D; ++d) out[d] /= l;
     *m_out = m;
@@ -148,9 +156,9 @@ static void attend_range(const uint16_t *qr, const uint16_t *k_cache, const uint
 /* O1 -- decode output.  out[s, h, :] = softmax(scale * q[s,h] . K_s) V_s over
  * the seq_lens[s] tokens of sequence s (seq_lens counts the current token,
  * RL.cu page, attention.cuh comment on seq_lens).  A zero length writes zeros. */
-int oracle_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                  const int32_t *block_tables, const int32_t *seq_lens,
-                  int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
+static int decode_impl(const uint16_t *q, kv_cache_t k_cache, kv_cache_t v_cache,
+                       const int32_t *block_tables, const int32_t *seq_lens,
+                       int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
     if (Hq % Hkv != 0) return 2;
     long pairs = (long)S * Hq;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -175,10 +183,10 @@ int oracle_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_
  * (section 2, "attention_partial") keeps the unnormalized weighted sum; the
  * normalized form stored here differs from it by the factor exp_sum, which the
  * merge multiplies back.  Partitions at or beyond ceil(L / P) are not written. */
-int oracle_decode_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                           const int32_t *block_tables, const int32_t *seq_lens,
-                           int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
-                           int P, int NP, double *max_logits, double *exp_sums, double *tmp_out) {
+static int partials_impl(const uint16_t *q, kv_cache_t k_cache, kv_cache_t v_cache,
+                         const int32_t *block_tables, const int32_t *seq_lens,
+                         int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
+                         int P, int NP, double *max_logits, double *exp_sums, double *tmp_out) {
     if (Hq % Hkv != 0 || P <= 0) return 2;
     long work = (long)S * Hq * NP;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -208,6 +216,41 @@ int oracle_decode_partials(const uint16_t *q, const uint16_t *k_cache, const uin
         free(z);
     }
     return 0;
+}
+
+int oracle_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                  const int32_t *block_tables, const int32_t *seq_lens,
+                  int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
+    kv_cache_t k = {k_cache, NULL}, v = {v_cache, NULL};
+    return decode_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, out);
+}
+
+int oracle_decode_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                           const int32_t *block_tables, const int32_t *seq_lens,
+                           int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
+                           int P, int NP, double *max_logits, double *exp_sums, double *tmp_out) {
+    kv_cache_t k = {k_cache, NULL}, v = {v_cache, NULL};
+    return partials_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, P, NP,
+                         max_logits, exp_sums, tmp_out);
+}
+
+/* O1 and O2 over fp64 caches: the same definitions with K and V given as
+ * values (a dequantized FP8 cache, see oracle_fp8_dequant). */
+int oracle_decode_f64kv(const uint16_t *q, const double *k_cache, const double *v_cache,
+                        const int32_t *block_tables, const int32_t *seq_lens,
+                        int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
+    kv_cache_t k = {NULL, k_cache}, v = {NULL, v_cache};
+    return decode_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, out);
+}
+
+int oracle_decode_partials_f64kv(const uint16_t *q, const double *k_cache, const double *v_cache,
+                                 const int32_t *block_tables, const int32_t *seq_lens,
+                                 int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
+                                 int P, int NP, double *max_logits, double *exp_sums,
+                                 double *tmp_out) {
+    kv_cache_t k = {NULL, k_cache}, v = {NULL, v_cache};
+    return partials_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, P, NP,
+                         max_logits, exp_sums, tmp_out);
 }
 
 /* O3 -- cross-partition merge (BI-V100 design page, section 2 "combine" and
@@ -253,11 +296,12 @@ int oracle_reduce(const double *max_logits, const double *exp_sums, const double
  * sits at absolute position c + j with c = L - n, and it attends to keys
  * t <= c + j (the causal rule of the RL.cu page's prefill kernel, aligned to
  * the end of the context). */
-int oracle_prefill(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+int oracle_prefill(const uint16_t *q, const uint16_t *k_bits, const uint16_t *v_bits,
                    const int32_t *block_tables, const int32_t *seq_lens, const int32_t *cu_seqlens,
                    int S, int total_q, int Hq, int Hkv, int D, int bs, int mbps, float scale,
                    double *out) {
     if (Hq % Hkv != 0) return 2;
+    kv_cache_t k_cache = {k_bits, NULL}, v_cache = {v_bits, NULL};
     long work = (long)total_q * Hq;
     for (long i = 0; i < work * D; ++i) out[i] = 0.0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -291,5 +335,164 @@ int oracle_prefill(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v
                      out + w * D, &m, &l);
         free(z);
     }
+    return 0;
+}
+
+/* ---- KV cache writes ------------------------------------------------------ */
+
+/* KV append: the cache write that comes before decode and prefill (the AstrAI
+ * page's backend layer "owns KV cache writes and reads"; the B200 page's paged
+ * KV cache read/write).  Sequence s owns new rows [cu[s], cu[s+1]) of k_new /
+ * v_new ([num_tokens, H_kv, D]); they are the last n = cu[s+1] - cu[s] of its
+ * seq_lens[s] tokens, so row j goes to position c + j with c = L - n: block
+ * table entry (c + j) / bs, slot (c + j) % bs -- the placement of the prefill
+ * rows above.  k_cache / v_cache are updated in place; nothing else changes.
+ * Returns 2 if some sequence has fewer tokens than new rows. */
+static long append_position(int c, int j) {
+#if ORACLE_MUTANT == 17
+    return (long)c + j + 1;
+#else
+    return (long)c + j;
+#endif
+}
+
+int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *block_tables,
+                     const int32_t *seq_lens, const int32_t *cu_seqlens, int S, int Hkv, int D,
+                     int bs, int mbps, uint16_t *k_cache, uint16_t *v_cache) {
+    for (int s = 0; s < S; ++s) {
+        int n = cu_seqlens[s + 1] - cu_seqlens[s];
+        int c = seq_lens[s] - n;
+        if (c < 0) return 2;
+        for (int j = 0; j < n; ++j) {
+            long pos = append_position(c, j);
+            if (pos / bs >= mbps) continue;
+            for (int g = 0; g < Hkv; ++g) {
+                long dst = kv_row(block_tables, s, (int)pos, g, Hkv, bs, D, mbps);
+                long src = ((long)(cu_seqlens[s] + j) * Hkv + g) * D;
+                memcpy(k_cache + dst, k_new + src, sizeof(uint16_t) * (size_t)D);
+                memcpy(v_cache + dst, v_new + src, sizeof(uint16_t) * (size_t)D);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---- FP8 (E4M3) KV cache -------------------------------------------------- */
+
+/* Value of an OCP FP8 E4M3 ("e4m3fn") code: sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9;
+ * codes 0x7F and 0xFF are NaN; there are no infinities, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(int code) {
+    int sgn = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) {
+#if ORACLE_MUTANT == 18
+        v = 0.0; /* drops the subnormals */
+#else
+        v = m * ldexp(1.0, -9);
+#endif
+    } else {
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    }
+    return sgn ? -v : v;
+}
+
+/* The non-negative E4M3 code nearest to a >= 0: every finite magnitude code
+ * 0x00..0x7E is tried; on a tie the even code (even last mantissa bit) wins.
+ * Magnitudes past 448 land on 448. */
+static int e4m3_nearest(float a) {
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(oracle_e4m3_value(c) - (double)a);
+#if ORACLE_MUTANT == 15
+        if (d < bd || (d == bd && c > best)) { /* ties away from zero */
+#else
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+#endif
+            bd = d;
+            best = c;
+        }
+    }
+    return best;
+}
+
+#define E4M3_MAX 448.0f
+
+/* FP8 quantization of rows of D bf16 values, one dequant scale per row (the
+ * B200 page's "FP8 KV Quantize/Dequant" with a "per-position dequant scale":
+ * one scale per cached position and kv head).  For each row:
+ *   amax = max_d |x_d|;  scale = fp32(amax / 448);
+ *   code_d = sign(x_d) | nearest E4M3 magnitude to fp32(|x_d| / scale)
+ *   (ties to the even code, saturating at 448).
+ * Both divisions are single-precision, correctly rounded.  A row of zeros gets
+ * scale 0 and zero codes (with the sign of each zero).  Dequantized value =
+ * value(code) * scale. */
+static void quantize_row(const uint16_t *xr, int D, uint8_t *codes, float *scale) {
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float a = fabsf((float)bf16_to_double(xr[d]));
+        if (a > amax) amax = a;
+    }
+#if ORACLE_MUTANT == 16
+    float s = amax / 240.0f; /* another FP8 variant's largest magnitude */
+#else
+    float s = amax / E4M3_MAX;
+#endif
+    *scale = s;
+    for (int d = 0; d < D; ++d) {
+        float v = (float)bf16_to_double(xr[d]);
+        int sgn = signbit(v) ? 0x80 : 0;
+        int mag = s > 0.0f ? e4m3_nearest(fabsf(v) / s) : 0;
+        codes[d] = (uint8_t)(sgn | mag);
+    }
+}
+
+int oracle_quantize_fp8(const uint16_t *x, long rows, int D, uint8_t *codes, float *scales) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) quantize_row(x + r * D, D, codes + r * D, scales + r);
+    return 0;
+}
+
+/* value(code) * scale for rows of D codes with one scale each. */
+int oracle_fp8_dequant(const uint8_t *codes, const float *scales, long rows, int D, double *out) {
+    for (long r = 0; r < rows; ++r)
+        for (int d = 0; d < D; ++d)
+            out[r * D + d] = oracle_e4m3_value(codes[r * D + d]) * (double)scales[r];
+    return 0;
+}
+
+/* KV append into an FP8 cache: each new (token, kv head) row of K and of V is
+ * quantized as in oracle_quantize_fp8 and written with its scale to the same
+ * position oracle_kv_append uses.  Caches: codes [num_blocks, H_kv, bs, D],
+ * scales [num_blocks, H_kv, bs]. */
+int oracle_kv_append_fp8(const uint16_t *k_new, const uint16_t *v_new, const int32_t *block_tables,
+                         const int32_t *seq_lens, const int32_t *cu_seqlens, int S, int Hkv, int D,
+                         int bs, int mbps, uint8_t *k_cache, uint8_t *v_cache, float *k_scales,
+                         float *v_scales) {
+    uint8_t *row = (uint8_t *)malloc((size_t)D);
+    for (int s = 0; s < S; ++s) {
+        int n = cu_seqlens[s + 1] - cu_seqlens[s];
+        int c = seq_lens[s] - n;
+        if (c < 0) { free(row); return 2; }
+        for (int j = 0; j < n; ++j) {
+            long pos = append_position(c, j);
+            if (pos / bs >= mbps) continue;
+            for (int g = 0; g < Hkv; ++g) {
+                long dst = kv_row(block_tables, s, (int)pos, g, Hkv, bs, D, mbps);
+                long src = ((long)(cu_seqlens[s] + j) * Hkv + g) * D;
+                float sc;
+                quantize_row(k_new + src, D, row, &sc);
+                memcpy(k_cache + dst, row, (size_t)D);
+                k_scales[dst / D] = sc;
+                quantize_row(v_new + src, D, row, &sc);
+                memcpy(v_cache + dst, row, (size_t)D);
+                v_scales[dst / D] = sc;
+            }
+        }
+    }
+    free(row);
     return 0;
 }

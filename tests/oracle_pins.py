@@ -348,6 +348,206 @@ def pin_tile_map_golden(orc):
     assert b == g["q_tile_to_batch"] and i == g["q_tile_to_index"], (b, i)
 
 
+# --------------------------------------------------------------------------
+# KV append (the cache write before decode / prefill)
+# --------------------------------------------------------------------------
+def _append_problem(seed, Hkv, D, lens, n_new, bs=16):
+    """Contiguous K/V for every sequence, paged by the test; the last n_new[s]
+    rows of sequence s are the rows to append."""
+    rng = np.random.default_rng(seed)
+    kc = [rand_bits(rng, (L, Hkv, D)) for L in lens]
+    vc = [rand_bits(rng, (L, Hkv, D)) for L in lens]
+    kcache, vcache, bt = page_contiguous(kc, vc, bs, rng)
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(n_new)
+    k_new = np.concatenate([kc[s][L - n:] for s, (L, n) in enumerate(zip(lens, n_new))])
+    v_new = np.concatenate([vc[s][L - n:] for s, (L, n) in enumerate(zip(lens, n_new))])
+    return kc, vc, kcache, vcache, bt, np.asarray(lens, np.int32), cu, k_new, v_new
+
+
+def _slots_of_new_rows(bt, lens, n_new, bs):
+    """(block, slot) of every appended position, from the test's own paging."""
+    out = []
+    for s, (L, n) in enumerate(zip(lens, n_new)):
+        for t in range(L - n, L):
+            out.append((int(bt[s, t // bs]), t % bs))
+    return out
+
+
+def pin_kv_append_refills_erased_rows(orc):
+    """Erase the last rows of each sequence from a paged cache, append them back
+    from the contiguous rows: the cache must come back bit for bit (rows of
+    sequences with nothing to append, and every other slot, untouched)."""
+    lens, n_new, bs = [37, 16, 1, 70, 5], [5, 16, 1, 0, 3], 16
+    kc, vc, kcache, vcache, bt, sl, cu, k_new, v_new = _append_problem(61, 2, 8, lens, n_new)
+    k_er, v_er = kcache.copy(), vcache.copy()
+    for b, t in _slots_of_new_rows(bt, lens, n_new, bs):
+        k_er[b, :, t] = 0x7FC0  # NaN bits: any row left unwritten shows
+        v_er[b, :, t] = 0x7FC0
+    k2, v2 = orc.kv_append(k_new, v_new, bt, sl, cu, k_er, v_er)
+    assert np.array_equal(k2, kcache) and np.array_equal(v2, vcache), "append did not restore the cache"
+    b, t = _slots_of_new_rows(bt, lens, n_new, bs)[0]
+    assert k_er[b, 0, t, 0] == 0x7FC0, "the input caches must not be modified in place"
+
+
+# --------------------------------------------------------------------------
+# FP8 (OCP E4M3) KV cache
+# --------------------------------------------------------------------------
+def _e4m3_half_ulp(y):
+    """Half the E4M3 spacing at magnitude y (spacing 2^-9 below 2^-6, else 2^(e-3))."""
+    if y < 2.0 ** -6:
+        return 2.0 ** -10
+    return 2.0 ** (math.floor(math.log2(y)) - 4)
+
+
+def pin_e4m3_values_match_the_specification(orc):
+    g = json.load(open(os.path.join(HERE, "golden", "e4m3_ocp_facts.json")))
+    for code, v in g["values"].items():
+        got = orc.e4m3_value(int(code, 16))
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), (code, got, v)
+    for code in g["nan_codes"]:
+        assert math.isnan(orc.e4m3_value(int(code, 16))), code
+    pos = [orc.e4m3_value(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:])), "magnitudes must increase with the code"
+    assert sum(1 for v in pos if v > 0) == g["finite_positive_codes"]
+    assert max(pos) == g["max_finite"]
+    for c in range(0x7F):
+        assert orc.e4m3_value(c | 0x80) == -orc.e4m3_value(c)
+
+
+def pin_fp8_quantize_ties_to_even(orc):
+    """Rows whose largest magnitude is 448 get scale 1, so each x / scale is x
+    itself: exact midpoints between neighbouring codes must take the even code."""
+    x = np.array([[448.0, 1.0625, 1.1875, 1.5 * 2 ** -9, 2.0 ** -10, 432.0, 1.078125, -1.0625]],
+                 dtype=np.float32)
+    codes, scales = orc.quantize_fp8(f32_to_bf16_bits(x))
+    assert scales[0] == 1.0, scales
+    want = [0x7E, 0x38, 0x3A, 0x02, 0x00, 0x7E, 0x39, 0xB8]
+    assert codes[0].tolist() == want, [hex(c) for c in codes[0]]
+
+
+def pin_fp8_quantize_round_trip(orc):
+    """Rows made of E4M3 values times 2^k with one entry at +-448 * 2^k: the
+    scale is 2^k exactly and every code comes back unchanged."""
+    rng = np.random.default_rng(62)
+    for k in (-8, 0, 3):
+        codes0 = rng.integers(0, 0x7F, size=(6, 32)).astype(np.uint8)
+        codes0 |= (rng.integers(0, 2, size=codes0.shape) * 0x80).astype(np.uint8)
+        codes0[:, 5] = 0x7E | (codes0[:, 5] & 0x80)
+        vals = np.array([[orc.e4m3_value(int(c)) * 2.0 ** k for c in row] for row in codes0],
+                        dtype=np.float32)
+        bits = f32_to_bf16_bits(vals)
+        assert np.array_equal(bf16_bits_to_f32(bits), vals), "test values must be bf16-exact"
+        codes, scales = orc.quantize_fp8(bits)
+        assert np.all(scales == np.float32(2.0 ** k)), scales
+        # +-0 keep their sign bit; every other code is reproduced exactly
+        assert np.array_equal(codes, codes0), np.argwhere(codes != codes0)[:4]
+
+
+def pin_fp8_quantize_error_bound(orc):
+    """Random rows: each dequantized value is within half an E4M3 spacing (of
+    x / scale, times the scale) of x, and the row maximum maps to +-448."""
+    rng = np.random.default_rng(63)
+    x = (rng.standard_normal((40, 64)) * np.exp(rng.uniform(-6, 6, size=(40, 1)))).astype(np.float32)
+    bits = f32_to_bf16_bits(x)
+    xv = bf16_bits_to_f32(bits).astype(np.float64)
+    codes, scales = orc.quantize_fp8(bits)
+    deq = orc.fp8_dequant(codes, scales)
+    for r in range(x.shape[0]):
+        s = float(scales[r])
+        amax = float(np.max(np.abs(xv[r])))
+        assert abs(s - amax / 448.0) <= amax / 448.0 * 2.0 ** -23
+        j = int(np.argmax(np.abs(xv[r])))
+        assert codes[r, j] & 0x7F == 0x7E
+        for d in range(x.shape[1]):
+            y = abs(xv[r, d]) / s
+            bound = _e4m3_half_ulp(y) * s * (1 + 1e-6) + amax * 2.0 ** -22
+            assert abs(deq[r, d] - xv[r, d]) <= bound, (r, d, deq[r, d], xv[r, d])
+
+
+def pin_fp8_quantize_zero_row(orc):
+    x = np.zeros((2, 16), np.float32)
+    x[1] = -0.0
+    codes, scales = orc.quantize_fp8(f32_to_bf16_bits(x))
+    assert scales.tolist() == [0.0, 0.0]
+    assert codes[0].tolist() == [0] * 16 and codes[1].tolist() == [0x80] * 16
+
+
+def _pow2_fp8_cache(rng, shape):
+    """FP8 codes with power-of-two scales: every dequantized value is bf16-exact."""
+    codes = rng.integers(0, 0x7F, size=shape).astype(np.uint8)
+    codes |= (rng.integers(0, 2, size=shape) * 0x80).astype(np.uint8)
+    scales = (2.0 ** rng.integers(-9, -3, size=shape[:-1])).astype(np.float32)
+    return codes, scales
+
+
+def pin_fp8_decode_equals_bf16_decode_when_exact(orc):
+    """With power-of-two scales the dequantized cache is exactly a bf16 cache:
+    the FP8 decode (and its partials) must equal the bf16 decode bit for bit."""
+    rng = np.random.default_rng(64)
+    Hq, Hkv, D, bs = 8, 2, 16, 16
+    lens = np.array([1, 40, 100], np.int32)
+    nb = 20
+    kq, ks = _pow2_fp8_cache(rng, (nb, Hkv, bs, D))
+    vq, vs = _pow2_fp8_cache(rng, (nb, Hkv, bs, D))
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.stack([perm[:7], perm[7:14], perm[13:20]])
+    q = rand_bits(rng, (3, Hq, D))
+    kd, vd = orc.fp8_dequant(kq, ks), orc.fp8_dequant(vq, vs)
+    kb, vb = f32_to_bf16_bits(kd.astype(np.float32)), f32_to_bf16_bits(vd.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(kb).astype(np.float64), kd)
+    scale = np.float32(0.25)
+    got = orc.decode_fp8(q, kq, vq, ks, vs, bt, lens, Hkv, scale)
+    ref = orc.decode(q, kb, vb, bt, lens, Hkv, scale)
+    assert np.array_equal(got, ref)
+    gp = orc.decode_partials_fp8(q, kq, vq, ks, vs, bt, lens, Hkv, scale, 32)
+    rp = orc.decode_partials(q, kb, vb, bt, lens, Hkv, scale, 32)
+    for a, b in zip(gp, rp):
+        assert np.array_equal(np.nan_to_num(a), np.nan_to_num(b))
+
+
+def pin_fp8_decode_single_token(orc):
+    """One cached token: the output is that token's dequantized value row."""
+    rng = np.random.default_rng(65)
+    kq, ks = _pow2_fp8_cache(rng, (3, 1, 16, 32))
+    vq = rng.integers(0, 0x7F, size=(3, 1, 16, 32)).astype(np.uint8)
+    vs = np.array([[[0.013] * 16]] * 3, np.float32)
+    bt = np.array([[2], [0]], np.int32)
+    q = rand_bits(rng, (2, 4, 32))
+    out = orc.decode_fp8(q, kq, vq, ks, vs, bt, np.array([1, 1], np.int32), 1, np.float32(0.2))
+    deq = orc.fp8_dequant(vq, vs)
+    for s, blk in enumerate((2, 0)):
+        for h in range(4):
+            assert np.array_equal(out[s, h], deq[blk, 0, 0]), (s, h)
+
+
+def pin_fp8_kv_append_refills_erased_rows(orc):
+    """FP8 append of the last rows of each sequence equals those rows quantized
+    one by one and paged by the test, bit for bit (codes and scales)."""
+    lens, n_new, bs = [37, 16, 1, 70], [5, 16, 1, 0], 16
+    Hkv, D = 2, 16
+    kc, vc, kcache, vcache, bt, sl, cu, k_new, v_new = _append_problem(66, Hkv, D, lens, n_new)
+    nb = kcache.shape[0]
+    k8 = np.full((nb, Hkv, bs, D), 0x7F, np.uint8)
+    v8 = np.full((nb, Hkv, bs, D), 0x7F, np.uint8)
+    ksc = np.full((nb, Hkv, bs), np.nan, np.float32)
+    vsc = np.full((nb, Hkv, bs), np.nan, np.float32)
+    k2, v2, ks2, vs2 = orc.kv_append_fp8(k_new, v_new, bt, sl, cu, k8, v8, ksc, vsc)
+    ek, ev, eks, evs = k8.copy(), v8.copy(), ksc.copy(), vsc.copy()
+    row = 0
+    for s, (L, n) in enumerate(zip(lens, n_new)):
+        for t in range(L - n, L):
+            b, slot = int(bt[s, t // bs]), t % bs
+            for g in range(Hkv):
+                c, sc = orc.quantize_fp8(k_new[row, g][None])
+                ek[b, g, slot], eks[b, g, slot] = c[0], sc[0]
+                c, sc = orc.quantize_fp8(v_new[row, g][None])
+                ev[b, g, slot], evs[b, g, slot] = c[0], sc[0]
+            row += 1
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+    assert np.array_equal(ks2, eks, equal_nan=True) and np.array_equal(vs2, evs, equal_nan=True)
+
+
 PINS: Dict[str, Callable] = {name: fn for name, fn in sorted(globals().items())
                              if name.startswith("pin_") and callable(fn)}
 

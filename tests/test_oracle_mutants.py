@@ -4,7 +4,9 @@ Each mutant is the oracle source compiled with ORACLE_MUTANT=k (a dropped
 scale, a wrong GQA head map, an extra or shifted slot, a flipped exponent sign,
 K used as V, a dropped denominator term, unnormalized partials, overlapping
 partitions, a merge without exp_sum weights, a dropped causal diagonal,
-top-left causal alignment, a shifted query row, a transposed query index).
+top-left causal alignment, a shifted query row, a transposed query index,
+FP8 ties away from zero, a wrong FP8 scale, a late append position, FP8
+subnormals dropped).
 Every build runs the pin suite in a child process (a mutant may crash); the
 test requires at least one failing pin or a crash for each.
 """
@@ -32,6 +34,10 @@ MUTANTS = {
     12: "causal mask aligned top-left",
     13: "query row shifted",
     14: "query index transposed",
+    15: "FP8 ties rounded away from zero",
+    16: "FP8 scale from the wrong largest magnitude (240)",
+    17: "append one position late",
+    18: "FP8 subnormals read as zero",
 }
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
