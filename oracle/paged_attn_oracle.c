@@ -399,14 +399,27 @@ double oracle_e4m3_value(int code) {
     return sgn ? -v : v;
 }
 
+/* The 256 code values, computed once from oracle_e4m3_value (a cache of the
+ * definition above, filled before any parallel region reads it). */
+static double e4m3_table_[256];
+static int e4m3_table_ready_ = 0;
+static const double *e4m3_table(void) {
+    if (!e4m3_table_ready_) {
+        for (int c = 0; c < 256; ++c) e4m3_table_[c] = oracle_e4m3_value(c);
+        e4m3_table_ready_ = 1;
+    }
+    return e4m3_table_;
+}
+
 /* The non-negative E4M3 code nearest to a >= 0: every finite magnitude code
  * 0x00..0x7E is tried; on a tie the even code (even last mantissa bit) wins.
  * Magnitudes past 448 land on 448. */
 static int e4m3_nearest(float a) {
+    const double *val = e4m3_table_;
     int best = 0;
     double bd = INFINITY;
     for (int c = 0; c <= 0x7E; ++c) {
-        double d = fabs(oracle_e4m3_value(c) - (double)a);
+        double d = fabs(val[c] - (double)a);
 #if ORACLE_MUTANT == 15
         if (d < bd || (d == bd && c > best)) { /* ties away from zero */
 #else
@@ -451,6 +464,7 @@ static void quantize_row(const uint16_t *xr, int D, uint8_t *codes, float *scale
 }
 
 int oracle_quantize_fp8(const uint16_t *x, long rows, int D, uint8_t *codes, float *scales) {
+    e4m3_table();
 #pragma omp parallel for schedule(static)
     for (long r = 0; r < rows; ++r) quantize_row(x + r * D, D, codes + r * D, scales + r);
     return 0;
@@ -458,9 +472,11 @@ int oracle_quantize_fp8(const uint16_t *x, long rows, int D, uint8_t *codes, flo
 
 /* value(code) * scale for rows of D codes with one scale each. */
 int oracle_fp8_dequant(const uint8_t *codes, const float *scales, long rows, int D, double *out) {
+    const double *val = e4m3_table();
+#pragma omp parallel for schedule(static)
     for (long r = 0; r < rows; ++r)
         for (int d = 0; d < D; ++d)
-            out[r * D + d] = oracle_e4m3_value(codes[r * D + d]) * (double)scales[r];
+            out[r * D + d] = val[codes[r * D + d]] * (double)scales[r];
     return 0;
 }
 
@@ -472,6 +488,7 @@ int oracle_kv_append_fp8(const uint16_t *k_new, const uint16_t *v_new, const int
                          const int32_t *seq_lens, const int32_t *cu_seqlens, int S, int Hkv, int D,
                          int bs, int mbps, uint8_t *k_cache, uint8_t *v_cache, float *k_scales,
                          float *v_scales) {
+    e4m3_table();
     uint8_t *row = (uint8_t *)malloc((size_t)D);
     for (int s = 0; s < S; ++s) {
         int n = cu_seqlens[s + 1] - cu_seqlens[s];
