@@ -120,6 +120,72 @@ int paged_attn_decode_fused(const void *q, const void *k_cache, const void *v_ca
                             void *stream);
 
 /*
+ * Paged GQA decode over an FP8 KV cache (the B200 page, "Stage D: FP8 Paged KV
+ * Gather": FP8 codes gathered through the block table, a per-position dequant
+ * scale applied after the gather).  Same computation, arguments, partials and
+ * status codes as paged_attn_decode, with K and V taken as
+ *   K[blk, h, slot, d] = e4m3(k_cache[blk, h, slot, d]) * k_scales[blk, h, slot]
+ * (and V likewise), where
+ *   k_cache, v_cache   uint8 [num_blocks, H_kv, block_size, D]  OCP FP8 E4M3
+ *                      codes ("e4m3fn": bias 7, no infinities, 0x7F/0xFF NaN)
+ *   k_scales, v_scales fp32  [num_blocks, H_kv, block_size]     dequant scales
+ * as paged_attn_kv_append_fp8 writes them.  Slots past a sequence's length may
+ * hold anything (NaN included); they are never used.  Partials merge with
+ * paged_attn_decode_reduce.  k_cache, v_cache, k_scales and v_scales must be
+ * 16-byte aligned.
+ */
+int paged_attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                          const float *k_scales, const float *v_scales,
+                          const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, int max_blocks_per_seq, float scale, int partition_size,
+                          void *out, float *max_logits, float *exp_sums, float *tmp_out,
+                          int max_num_partitions, void *stream);
+
+/*
+ * KV append: writes the K/V rows of new tokens into their cache slots -- the
+ * cache write before decode and prefill (the AstrAI page's backend layer "owns
+ * KV cache writes and reads").  Sequence s owns rows [cu_seqlens[s],
+ * cu_seqlens[s+1]) of k_new / v_new (bf16 [num_tokens, H_kv, D]); they are the
+ * LAST n = cu[s+1] - cu[s] of its seq_lens[s] tokens (seq_lens already counts
+ * them), so row j goes to position c + j, c = seq_lens[s] - n: block
+ * block_tables[s, (c + j) / block_size], slot (c + j) % block_size -- where
+ * paged_attn_prefill_ragged reads its rows; a decode step has n = 1.
+ *   k_cache, v_cache  bf16 [num_blocks, H_kv, block_size, D], updated in place
+ *                     (only the new rows' slots are written).
+ * max_new_tokens must be >= every n (it sizes the launch) and num_tokens must
+ * equal cu_seqlens[num_seqs]; seq_lens[s] >= n and valid block ids for the
+ * written positions are required (device values, not checked).  Two rows
+ * written to the same slot (a block shared by two sequences) race.
+ * num_seqs == 0 or num_tokens == 0 is a no-op.  Status codes as for decode.
+ */
+int paged_attn_kv_append(const void *k_new, const void *v_new, const int32_t *block_tables,
+                         const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs,
+                         int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
+                         int block_size, int num_blocks, int max_blocks_per_seq, void *k_cache,
+                         void *v_cache, void *stream);
+
+/*
+ * KV append into an FP8 cache (the B200 page, "FP8 KV Quantize/Dequant", with
+ * its per-position dequant scale): the same rows and placement as
+ * paged_attn_kv_append, each (token, kv head) row of K and of V quantized on
+ * its own:
+ *   amax = max_d |x_d|,  scale = amax / 448  (fp32, correctly rounded),
+ *   code_d = sign(x_d) | the E4M3 magnitude nearest to |x_d| / scale (fp32,
+ *            correctly rounded), ties to the even code, saturating at 448;
+ * a row of zeros gets scale 0 and zero codes.  Writes the codes to
+ * k_cache / v_cache (uint8 [num_blocks, H_kv, block_size, D]) and the scales
+ * to k_scales / v_scales (fp32 [num_blocks, H_kv, block_size]); dequantized
+ * value = e4m3(code) * scale.  All four must be 16-byte aligned.
+ */
+int paged_attn_kv_append_fp8(const void *k_new, const void *v_new, const int32_t *block_tables,
+                             const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs,
+                             int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
+                             int block_size, int num_blocks, int max_blocks_per_seq,
+                             void *k_cache, void *v_cache, float *k_scales, float *v_scales,
+                             void *stream);
+
+/*
  * Ragged paged prefill with a causal mask.  Sequence s owns query rows
  * [cu_seqlens[s], cu_seqlens[s+1]) of q / out ([total_q, H_q, D]); its
  * n = cu[s+1] - cu[s] new tokens are the LAST n of its seq_lens[s] tokens,

@@ -136,10 +136,14 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
                   int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                   int max_blocks_per_seq, float scale, int partition_size, void *out,
                   float *max_logits, float *exp_sums, float *tmp_out, int max_num_partitions,
-                  int32_t *counters, void *stream) {
+                  int32_t *counters, void *stream, const float *k_scales = nullptr,
+                  const float *v_scales = nullptr) {
     int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
     if (st != PA_OK) return st;
+    const bool fp8 = k_scales != nullptr;
+    if (fp8 && !aligned16(k_scales)) return PA_ERR_ALIGNMENT;
+    if (fp8 && !aligned16(v_scales)) return PA_ERR_ALIGNMENT;
     if (!scale_ok(scale)) return PA_ERR_BAD_VALUE;
     if (partition_size < 0 || partition_size % kBlockSize != 0) return PA_ERR_BAD_SHAPE;
     int nparts = 1;
@@ -174,10 +178,86 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
     a.exp_sums = exp_sums;
     a.tmp_out = tmp_out;
     a.counters = counters;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
     a.stream = static_cast<hipStream_t>(stream);
-    return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    const hipError_t e = fp8 ? pa::launch_decode_fp8(a) : pa::launch_decode(a);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int append_common(const void *k_new, const void *v_new, const int32_t *block_tables,
+                  const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs, int num_tokens,
+                  int max_new_tokens, int num_kv_heads, int head_dim, int block_size,
+                  int num_blocks, int max_blocks_per_seq, void *k_cache, void *v_cache,
+                  float *k_scales, float *v_scales, bool fp8, void *stream) {
+    if (!k_new || !v_new || !block_tables || !seq_lens || !cu_seqlens || !k_cache || !v_cache)
+        return PA_ERR_NULL_POINTER;
+    if (fp8 && (!k_scales || !v_scales)) return PA_ERR_NULL_POINTER;
+    if (num_seqs < 0 || num_tokens < 0 || max_new_tokens < 0 || num_kv_heads <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || head_dim <= 0 || block_size <= 0)
+        return PA_ERR_BAD_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > kGridYZMax) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGNMENT;
+    if (fp8 && (!aligned16(k_scales) || !aligned16(v_scales))) return PA_ERR_ALIGNMENT;
+    if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PA_OK;
+    if (max_new_tokens > num_tokens) return PA_ERR_BAD_SHAPE;
+    pa::AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.cu_seqlens = cu_seqlens;
+    a.num_seqs = num_seqs;
+    a.max_new_tokens = max_new_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = fp8 ? pa::launch_kv_append_fp8(a) : pa::launch_kv_append(a);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 }  // namespace
+
+int paged_attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                          const float *k_scales, const float *v_scales,
+                          const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, int max_blocks_per_seq, float scale, int partition_size,
+                          void *out, float *max_logits, float *exp_sums, float *tmp_out,
+                          int max_num_partitions, void *stream) {
+    if (!k_scales || !v_scales) return PA_ERR_NULL_POINTER;
+    return decode_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                         partition_size, out, max_logits, exp_sums, tmp_out, max_num_partitions,
+                         nullptr, stream, k_scales, v_scales);
+}
+
+int paged_attn_kv_append(const void *k_new, const void *v_new, const int32_t *block_tables,
+                         const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs,
+                         int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
+                         int block_size, int num_blocks, int max_blocks_per_seq, void *k_cache,
+                         void *v_cache, void *stream) {
+    return append_common(k_new, v_new, block_tables, seq_lens, cu_seqlens, num_seqs, num_tokens,
+                         max_new_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_blocks_per_seq, k_cache, v_cache, nullptr, nullptr, false, stream);
+}
+
+int paged_attn_kv_append_fp8(const void *k_new, const void *v_new, const int32_t *block_tables,
+                             const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs,
+                             int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
+                             int block_size, int num_blocks, int max_blocks_per_seq,
+                             void *k_cache, void *v_cache, float *k_scales, float *v_scales,
+                             void *stream) {
+    return append_common(k_new, v_new, block_tables, seq_lens, cu_seqlens, num_seqs, num_tokens,
+                         max_new_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_blocks_per_seq, k_cache, v_cache, k_scales, v_scales, true, stream);
+}
 
 int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,

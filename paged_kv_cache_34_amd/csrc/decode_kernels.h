@@ -1,0 +1,1015 @@
+// Paged GQA decode kernels for gfx950 (CDNA4): the split-KV partition kernel
+// (bf16 or FP8 KV cache) and the cross-partition merge kernels.
+//
+// What is computed (BI-V100 paged-attention design page, section 1 "Problem
+// Definition"; block-table walk of the RL.cu "Add Cuda Kernel" page's paged
+// decode kernel): for each sequence and query head, softmax(scale * q . K^T) V
+// over the sequence's tokens, whose K/V rows live in 16-token physical blocks
+// named by the block table.  With an FP8 cache (the B200 page, "Stage D: FP8
+// Paged KV Gather"), K and V are OCP E4M3 codes with one dequant scale per
+// (position, kv head), applied after the gather.
+//
+// Work decomposition (the BI-V100 page's section 4 GQA grouping and section 6
+// two-phase launch, re-designed for wave64 and MFMA):
+//   * a work item is (sequence, kv head, partition of P tokens), processed by
+//     one workgroup of NW waves that take the partition's 16-token blocks
+//     round-robin, so one K/V load serves all G query heads of the kv head;
+//   * QK^T of a block is v_mfma_f32_16x16x32_bf16 with the block's K tile as
+//     the A operand, loaded straight from HBM into the operand layout, and the
+//     G query rows as the B operand; the result S^T leaves lane l with the
+//     scores of head l % 16 for 4 tokens;
+//   * the online softmax runs on that layout: per-head block max over the 4
+//     lane groups with permlane swaps, a lazy running max (rescale only when a
+//     block's max exceeds it by more than 2^8), the exact max kept separately
+//     for the partial record;
+//   * PV is O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: V^T comes from the
+//     row-major V tile staged in LDS through transposed reads, P^T is the
+//     lane's own probabilities;
+//   * at the end the waves are merged in LDS with the combine rule of the
+//     BI-V100 page (section 2, "combine"), in a fixed order (deterministic).
+// Every step depends only on logical token positions, so permuting physical
+// blocks (with the table updated) gives bit-identical output.
+#pragma once
+
+#include "pa_common.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;        // tokens per physical KV block
+constexpr float kLazyTau = 8.0f;  // log2 headroom of the lazy running max
+// Fourth word of a raw buffer descriptor on the GFX9 family (32-bit data, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
+template <int D, int G, int NW>
+struct DecodeShape {
+    static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+    static_assert(G >= 1 && G <= 16, "GQA group");
+    static constexpr int NJ = D / 32;            // K chunk loads per lane = S^T k-steps
+    static constexpr int NDT = D / 16;           // 16-dim tiles of O^T
+    static constexpr int LPT = D / 8;            // lanes per token row in the V layout
+    static constexpr int TPI = 64 / LPT;         // tokens per V load instruction
+    static constexpr int VROW = D + 16;          // bf16 per staged V row (32-byte pad)
+    static constexpr int STAGE_FLOATS = NW * kBlock * VROW / 2;
+    static constexpr int RED_FLOATS = NW * G * D;
+    static constexpr int MAIN_FLOATS = RED_FLOATS > STAGE_FLOATS ? RED_FLOATS : STAGE_FLOATS;
+    static constexpr int STAT_FLOATS = 3 * NW * 16;
+};
+
+// Kernel argument block (validated on the host).
+struct DecodeParams {
+    const uint16_t *q, *k_cache, *v_cache;
+    const int32_t *block_tables, *seq_lens;
+    int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
+    float scale_log2;
+    int partition_size, max_num_partitions;
+    uint16_t *out;
+    float *max_logits, *exp_sums, *tmp_out;
+    int *counters;  // fused merge: one arrival counter per (sequence, kv head); null = no merge
+    // FP8 cache: dequant multipliers [num_blocks, H_kv, 16] (k_cache / v_cache
+    // then hold E4M3 codes [num_blocks, H_kv, 16, D]); null for a bf16 cache
+    const float *k_scales, *v_scales;
+};
+
+// 16-byte words per lane of one ring slot: the K (or V) tile, plus, for an
+// FP8 cache, the dequant scales of the lane's 4 score tokens.
+template <int D, bool FP8>
+struct KvWords {
+    static constexpr int N = FP8 ? D / 64 + 1 : D / 32;
+};
+
+// Two E4M3 codes (bytes 0, 1 of w, or 2, 3 when HI) -> two bf16, exactly
+// (every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Eight E4M3 codes (two dwords) -> eight bf16 (an MFMA operand).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    return u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
+                 e4m3x2_to_bf16x2<true>(w1)};
+}
+
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// One work item: partition `part` of kv head `kvh` of sequence `seq` (the whole
+// sequence when partition_size == 0), processed by the NW waves of the
+// calling workgroup; `lds` is the workgroup's scratch (DecodeShape floats).
+//
+// Per 16-token tile a wave computes, with the MFMA lane layouts
+// (col = lane % 16, grp = lane / 16):
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = K tile straight from HBM,
+//                  lane: token col, 16-byte chunk 4j + grp; B = the query rows)
+//                 -> lane holds scores of head col for tokens 4 grp + i;
+//   online softmax per head (block max over the 4 lane groups with permlane
+//   swaps, lazy running max);
+//   O^T += V^T P^T (v_mfma_f32_16x16x16_bf16; A = V^T read from the staged
+//                  row-major V tile with ds_read_b64_tr_b16, B = the lane's own
+//                  probabilities, split into bf16 high and low parts so the
+//                  product keeps ~16 mantissa bits) -> lane holds dims
+//                  16 dt + 4 grp + i of head col.
+// The probabilities never leave the lane that computed them, and V is never
+// converted on the VALU.
+// Partial-record element stores: plain, or agent-scope (coherent across the
+// XCDs' L2 caches) when the fused merge of another workgroup will read them.
+__device__ __forceinline__ void store_partial(float *p, float v, bool coherent) {
+    if (coherent)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+__device__ __forceinline__ float load_partial(float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A work item as one wave of the workgroup sees it: partition `part` of kv
+// head `kvh` of sequence `seq` (the whole sequence when partition_size == 0;
+// `L` = seq_lens[seq]).  The wave takes the item's 16-token blocks wave,
+// wave + NW, ...; `ids` holds the block ids of its first 64 (one per lane).
+struct DecodeItem {
+    int seq, kvh, part, L;
+    int t_end, b_begin, my_nb, ids;
+};
+
+template <int NW>
+__device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq, int kvh, int part,
+                                                int L, int wave, int lane) {
+    DecodeItem it;
+    L = __builtin_amdgcn_readfirstlane(L);  // uniform (the compiler cannot see it when L comes from LDS)
+    const int P = prm.partition_size;
+    const int t_begin = P ? part * P : 0;
+    it.seq = seq;
+    it.kvh = kvh;
+    it.part = part;
+    it.L = L;
+    it.t_end = P ? min(L, t_begin + P) : L;
+    it.b_begin = t_begin / kBlock;
+    const int nb = (it.t_end + kBlock - 1) / kBlock - it.b_begin;
+    it.my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + it.b_begin + wave;
+    it.ids = (lane < min(64, it.my_nb)) ? bt_row[NW * lane] : 0;
+    return it;
+}
+
+// Workgroup barrier for LDS traffic only: unlike __syncthreads it does not
+// wait for the wave's outstanding global loads, so prefetched tiles stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Processes item `it` with the NW waves of the calling workgroup; `lds` is
+// the workgroup's scratch (DecodeShape floats).  `qb` (the item's query rows)
+// and the ring `kbuf`/`vbuf` (its first DEPTH tiles, tile j in slot j) are
+// either loaded here (`primed` false) or were issued by the previous item.
+// When `has_next`, the item issues the same for `nx` before its epilogue, so
+// the next item's first loads are in flight while this one merges its waves.
+// ONE_CHUNK: the caller guarantees at most 64 tiles per wave (NW * 1024
+// tokens per item), so the block ids are never reloaded inside the item.
+//
+// Per 16-token tile a wave computes, with the MFMA lane layouts
+// (col = lane % 16, grp = lane / 16):
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = K tile straight from HBM,
+//                  lane: token col, 16-byte chunk 4j + grp; B = the query rows)
+//                 -> lane holds scores of head col for tokens 4 grp + i;
+//   online softmax per head (block max over the 4 lane groups with permlane
+//   swaps, lazy running max);
+//   O^T += V^T P^T (v_mfma_f32_16x16x16_bf16; A = V^T read from the staged
+//                  row-major V tile with ds_read_b64_tr_b16, B = the lane's own
+//                  probabilities, split into bf16 high and low parts so the
+//                  product keeps ~16 mantissa bits) -> lane holds dims
+//                  16 dt + 4 grp + i of head col.
+// Lanes with col >= G carry a copy of head 0; their results are never stored.
+template <int D, int G, int NW, int DEPTH, bool ONE_CHUNK, bool FP8>
+__device__ __forceinline__ void decode_item(const DecodeParams &prm, const DecodeItem &it,
+                                            const DecodeItem &nx, bool has_next, bool primed,
+                                            u32x4 (&qb)[D / 32],
+                                            u32x4 (&kbuf)[DEPTH + 1][KvWords<D, FP8>::N],
+                                            u32x4 (&vbuf)[DEPTH + 1][KvWords<D, FP8>::N], float *lds) {
+    using S = DecodeShape<D, G, NW>;
+    constexpr int NJ = S::NJ, NDT = S::NDT, VROW = S::VROW;
+    constexpr int NW16 = KvWords<D, FP8>::N;      // words per ring slot
+    // V tile loads: a token row is LPT lanes of 16 bytes (8 bf16 or 16 E4M3
+    // codes); one load instruction covers TPI rows; NV loads per lane
+    constexpr int LPT = FP8 ? D / 16 : D / 8, TPI = 64 / LPT, NV = kBlock / TPI;
+    constexpr int NK = FP8 ? D / 64 : D / 32;     // K tile loads per lane
+    constexpr int EB = FP8 ? 1 : 2;               // bytes per cached element
+    const int num_q_heads = prm.num_q_heads;
+    const int partition_size = prm.partition_size, max_num_partitions = prm.max_num_partitions;
+    const float scale_log2 = prm.scale_log2;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    // (the item fields are wave-uniform; say so, since values carried around
+    // the persistent loop may sit in vector registers)
+    const int seq = __builtin_amdgcn_readfirstlane(it.seq), kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+    const int part = __builtin_amdgcn_readfirstlane(it.part), L = __builtin_amdgcn_readfirstlane(it.L);
+    const int t_end = __builtin_amdgcn_readfirstlane(it.t_end);
+    const int b_begin = __builtin_amdgcn_readfirstlane(it.b_begin);
+    const int my_nb = __builtin_amdgcn_readfirstlane(it.my_nb);
+    const int nx_kvh = __builtin_amdgcn_readfirstlane(nx.kvh);
+    const int nx_nb = __builtin_amdgcn_readfirstlane(nx.my_nb);
+    const int h0 = kvh * G;
+    const int col = lane & 15, grp = lane >> 4;
+    const int vcol = lane % LPT, vrow = lane / LPT;  // V load lane: 16-byte chunk vcol of row vrow
+
+    // query rows as the B operand of S^T: lane holds q[head col][chunk 4j + grp]
+    // (FP8: K step j = 2m + h holds dims 64m + 16 grp + 8h + 0..7, the order in
+    // which one 16-byte load of 16 codes arrives; the dot product is the same)
+    auto load_q = [&](int s, int g) {
+        const uint16_t *qrow = prm.q + ((long)s * num_q_heads + g * G + (col < G ? col : 0)) * D;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            qb[j] = load_u32x4(qrow + (FP8 ? 64 * (j >> 1) + 16 * grp + 8 * (j & 1) : (4 * j + grp) * 8));
+    };
+
+    const long tile = (long)kBlock * D * EB;       // bytes of one (block, kv head) tile
+    const long blk_stride = (long)prm.num_kv_heads * tile;
+    const char *kc = reinterpret_cast<const char *>(prm.k_cache);
+    const char *vc = reinterpret_cast<const char *>(prm.v_cache);
+    const char *kv_k = kc + kvh * tile, *kv_v = vc + kvh * tile;
+    const char *nx_k = kc + nx_kvh * tile, *nx_v = vc + nx_kvh * tile;
+    // bytes within a tile: K lane = (token col, chunk grp (+ 4j)); V lane = (row vrow, chunk vcol)
+    const int k_voff = FP8 ? col * D + 16 * grp : (col * D + grp * 8) * 2;
+    const int v_voff = (vrow * D * EB) + vcol * 16;
+    // FP8 scales: [num_blocks, H_kv, 16] floats, the lane's 4 score tokens 4 grp + 0..3
+    const float *ks_cur = FP8 ? prm.k_scales + kvh * kBlock : nullptr;
+    const float *vs_cur = FP8 ? prm.v_scales + kvh * kBlock : nullptr;
+    const float *ks_nx = FP8 ? prm.k_scales + nx_kvh * kBlock : nullptr;
+    const float *vs_nx = FP8 ? prm.v_scales + nx_kvh * kBlock : nullptr;
+    const long sc_stride = (long)prm.num_kv_heads * kBlock;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + b_begin + wave;
+
+    // per-wave V staging tile [16][VROW] bf16
+    uint16_t *vstage = reinterpret_cast<uint16_t *>(lds) + wave * kBlock * VROW;
+    uint16_t *vst_wr = vstage + vrow * VROW + vcol * (FP8 ? 16 : 8);
+    const uint16_t *vst_rd = vstage + (4 * grp + (col >> 2)) * VROW + 4 * (col & 3);
+
+    f32x4 oT[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, m_ex = -INFINITY, l_run = 0.f;
+
+    // Issues tile j of the current chunk (n tiles, block ids `ids` one per
+    // lane) into a ring slot with buffer loads whose descriptor covers exactly
+    // that tile.  In the item's last chunk the tiles past its end are the next
+    // item's first tiles, counted from the first multiple of DEPTH + 1 at or
+    // after n so that they land in ring slots 0, 1, ...; any other slot gets an
+    // empty descriptor, whose loads return zeros without touching memory.  All
+    // choices are wave-uniform and the loads unconditional, so the compiler's
+    // wait counts stay exact.
+    auto load_tile = [&](int ids, int j, int n, bool last, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
+        const int base = (n + DEPTH) / (DEPTH + 1) * (DEPTH + 1);
+        const int jn = j - base;
+        const bool cur = j < n;
+        const bool nxt = !cur && last && has_next && jn >= 0 && jn < min(64, nx_nb);
+        const long phys = cur ? __builtin_amdgcn_readlane(ids, j)
+                              : __builtin_amdgcn_readlane(nx.ids, nxt ? jn : 0);
+        const int bytes = (cur || nxt) ? (int)tile : 0;
+        const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? kv_k : nx_k) + phys * blk_stride),
+                                                           0, bytes, kBufferFlags);
+        const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? kv_v : nx_v) + phys * blk_stride),
+                                                           0, bytes, kBufferFlags);
+#pragma unroll
+        for (int j2 = 0; j2 < NK; ++j2)
+            kr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + j2 * 64, 0, 0));
+#pragma unroll
+        for (int j2 = 0; j2 < NV; ++j2)
+            vr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + j2 * TPI * D * EB, 0, 0));
+        if constexpr (FP8) {
+            const int sbytes = (cur || nxt) ? kBlock * 4 : 0;
+            const auto ksr = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? ks_cur : ks_nx) + phys * sc_stride),
+                                                               0, sbytes, kBufferFlags);
+            const auto vsr = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? vs_cur : vs_nx) + phys * sc_stride),
+                                                               0, sbytes, kBufferFlags);
+            kr[NK] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ksr, 16 * grp, 0, 0));
+            vr[NV] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vsr, 16 * grp, 0, 0));
+        }
+    };
+
+    auto compute_tile = [&](int i, const u32x4 (&kr)[NW16], const u32x4 (&vr)[NW16]) {
+        const int tb = (b_begin + wave + NW * i) * kBlock;  // logical index of slot 0
+        const bool tail = tb + kBlock > t_end;
+        // stage V as bf16 (FP8 codes converted exactly; token rows past the end
+        // are zeroed so stale slots never reach PV)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const bool dead = tail && tb + vrow + j * TPI >= t_end;
+            if constexpr (FP8) {
+                const u32x4 w = vr[j];
+                const u32x4 lo = dead ? u32x4{0u, 0u, 0u, 0u} : e4m3x8_to_bf16x8(w[0], w[1]);
+                const u32x4 hi = dead ? u32x4{0u, 0u, 0u, 0u} : e4m3x8_to_bf16x8(w[2], w[3]);
+                *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW) = lo;
+                *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW + 8) = hi;
+            } else {
+                *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW) = dead ? u32x4{0u, 0u, 0u, 0u} : vr[j];
+            }
+        }
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            u32x4 ka;
+            if constexpr (FP8)
+                ka = e4m3x8_to_bf16x8(kr[j >> 1][2 * (j & 1)], kr[j >> 1][2 * (j & 1) + 1]);
+            else
+                ka = kr[j];
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka),
+                                                         __builtin_bit_cast(bf16x8, qb[j]), st, 0, 0, 0);
+        }
+        float z[4];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            // (FP8: the K dequant scale of the token multiplies its score)
+            const float sk = FP8 ? __uint_as_float(kr[NK][i2]) * scale_log2 : scale_log2;
+            z[i2] = (tb + 4 * grp + i2 < t_end) ? st[i2] * sk : -INFINITY;
+            bm = fmaxf(bm, z[i2]);
+        }
+        bm = max_xor32(max_xor16(bm));
+        if (__any(bm > m_run + kLazyTau)) {
+            const float mn = fmaxf(m_run, bm);
+            const float al = fast_exp2(m_run - mn);
+            m_run = mn;
+            l_run *= al;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oT[dt] *= al;
+        }
+        m_ex = fmaxf(m_ex, bm);
+        float p[4];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) p[i2] = fast_exp2(z[i2] - m_run);
+        l_run += (p[0] + p[1]) + (p[2] + p[3]);
+        if constexpr (FP8) {
+            // the V dequant scale of each token weights its probability in PV
+            // (masked tokens: 0, whatever their unused scale slot holds)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2)
+                p[i2] = (tb + 4 * grp + i2 < t_end) ? p[i2] * __uint_as_float(vr[NV][i2]) : 0.f;
+        }
+        const uint32_t h01 = cvt_pk_bf16(p[0], p[1]), h23 = cvt_pk_bf16(p[2], p[3]);
+        const uint32_t l01 = cvt_pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+        const uint32_t l23 = cvt_pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+        const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+        const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+        wave_lds_sync();
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)(vst_rd + dt * 16));
+            oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, oT[dt], 0, 0, 0);
+            oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, oT[dt], 0, 0, 0);
+        }
+        wave_lds_sync();
+    };
+
+    if (!primed) {
+        load_q(seq, kvh);
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_tile(it.ids, d, min(64, my_nb), my_nb <= 64, kbuf[d], vbuf[d]);
+    }
+
+    // Tiles are processed in chunks of 64 whose block ids sit one per lane;
+    // within a chunk a ring of DEPTH + 1 register tiles keeps tile i + DEPTH
+    // in flight while tile i is consumed.
+    auto run_chunk = [&](int ids, int c0, int n, bool last) {
+        for (int i = 0; i < n; i += DEPTH + 1) {
+#pragma unroll
+            for (int u = 0; u <= DEPTH; ++u) {
+                load_tile(ids, i + u + DEPTH, n, last, kbuf[(u + DEPTH) % (DEPTH + 1)],
+                          vbuf[(u + DEPTH) % (DEPTH + 1)]);
+                if (i + u < n) compute_tile(c0 + i + u, kbuf[u], vbuf[u]);
+            }
+        }
+    };
+    if (ONE_CHUNK) {
+        run_chunk(it.ids, 0, my_nb, true);
+    } else {
+        for (int c0 = 0; c0 < my_nb; c0 += 64) {
+            const int n = min(64, my_nb - c0);
+            const bool last = c0 + 64 >= my_nb;
+            const int ids = c0 == 0 ? it.ids : ((lane < n) ? bt_row[NW * (c0 + lane)] : 0);
+            if (c0 > 0) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) load_tile(ids, d, n, last, kbuf[d], vbuf[d]);
+            }
+            run_chunk(ids, c0, n, last);
+        }
+    }
+    if (has_next) {
+        // a wave that streamed nothing has not issued the next item's tiles yet
+        if (my_nb == 0) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) load_tile(0, d, 0, true, kbuf[d], vbuf[d]);
+        }
+        load_q(__builtin_amdgcn_readfirstlane(nx.seq), nx_kvh);
+    }
+
+    // ---- per-wave totals -------------------------------------------------
+    // (the fused merge needs full barriers; otherwise LDS-only barriers keep
+    // the next item's loads in flight)
+    const bool fused = prm.counters != nullptr;
+    auto wg_sync = [&]() {
+        if (fused) __syncthreads();
+        else lds_barrier();
+    };
+    l_run = sum_xor32(sum_xor16(l_run));
+    wg_sync();  // every wave is done with its staging tile before the buffer is reused
+    float *red = lds;                      // [NW][G][D]
+    float *st_m = lds + S::MAIN_FLOATS;    // [NW][16] running max (log2 units)
+    float *st_x = st_m + NW * 16;          // [NW][16] exact max (log2 units)
+    float *st_l = st_x + NW * 16;          // [NW][16] exp-sum relative to running max
+    if (col < G) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<f32x4 *>(red + (wave * G + col) * D + 16 * dt + 4 * grp) = oT[dt];
+        if (grp == 0) {
+            st_m[wave * 16 + col] = m_run;
+            st_x[wave * 16 + col] = m_ex;
+            st_l[wave * 16 + col] = l_run;
+        }
+    }
+    wg_sync();
+
+    // ---- merge the waves (fixed order) and write ---------------------------
+    // The item writes bf16 output directly when it is the whole sequence
+    // (single pass, or the fused mode with one partition); otherwise its
+    // partial record.
+    const long row0 = (long)seq * num_q_heads + h0;
+    const int nparts = partition_size ? (L + partition_size - 1) / partition_size : 1;
+    const bool direct = partition_size == 0 || (fused && nparts == 1);
+    for (int e = tid; e < G * D; e += NW * 64) {
+        const int h = e / D, d = e % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, st_m[w * 16 + h]);
+        float lsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(st_m[w * 16 + h] - M);
+            lsum = fmaf(f, st_l[w * 16 + h], lsum);
+            o = fmaf(f, red[(w * G + h) * D + d], o);
+        }
+        o = o / lsum;
+        if (direct)
+            prm.out[(row0 + h) * D + d] = (uint16_t)f32_to_bf16_bits(o);
+        else
+            store_partial(prm.tmp_out + ((row0 + h) * max_num_partitions + part) * D + d, o, fused);
+    }
+    if (!direct && tid < G) {
+        const int h = tid;
+        float M = -INFINITY, X = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            M = fmaxf(M, st_m[w * 16 + h]);
+            X = fmaxf(X, st_x[w * 16 + h]);
+        }
+        float lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) lsum = fmaf(fast_exp2(st_m[w * 16 + h] - M), st_l[w * 16 + h], lsum);
+        store_partial(prm.max_logits + (row0 + h) * max_num_partitions + part, X * kLn2, fused);
+        store_partial(prm.exp_sums + (row0 + h) * max_num_partitions + part, lsum * fast_exp2(M - X), fused);
+    }
+    if (!direct && fused) {
+        // Fused cross-partition merge (the BI-V100 page, section 2 "Level 3":
+        // "or the last partition block"): publish the partial device-wide,
+        // count arrivals of the (sequence, kv head) partitions, and let the
+        // workgroup that completes the set merge them in partition order.
+        // The partial records were written with agent-scope (cross-XCD
+        // coherent) stores; each wave waits for its stores to complete, the
+        // barrier collects the waves, and only then is the arrival counted.
+        // The workgroup completing the set reads the records back with
+        // agent-scope loads, so no cache-wide writeback or invalidate is needed.
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        __syncthreads();
+        int *flag = reinterpret_cast<int *>(st_m);
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(prm.counters + (long)seq * prm.num_kv_heads + kvh, 1,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            flag[0] = (old == nparts - 1);
+        }
+        __syncthreads();
+        if (flag[0]) {
+            // The merge runs over (column, slot) pairs: a column is 4
+            // consecutive dims of one head; a column's SL slots take the
+            // partitions round-robin, 4 at a time with every load issued
+            // before any is used, each slot keeping a running max; then the
+            // slots are folded in LDS in slot order (deterministic).
+            constexpr int T = NW * 64;
+            constexpr int COLS = G * D / 4;
+            constexpr int SL = T / COLS >= 1 ? T / COLS : 1;
+            constexpr int MU = 4;
+            float *fold = lds;  // [SL][COLS][6]: max, weight sum, 4 accumulators
+            static_assert(SL * COLS * 6 <= S::MAIN_FLOATS, "merge fold fits the scratch");
+            for (int pr = tid; pr < COLS * SL; pr += T) {
+                const int c = pr % COLS, sl = pr / COLS;
+                const int h = c / (D / 4), d0 = 4 * (c % (D / 4));
+                float *mlr = prm.max_logits + (row0 + h) * max_num_partitions;
+                float *esr = prm.exp_sums + (row0 + h) * max_num_partitions;
+                float *tor = prm.tmp_out + (row0 + h) * max_num_partitions * (long)D + d0;
+                float m = -INFINITY, wsum = 0.f;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int p0 = sl; p0 < nparts; p0 += SL * MU) {
+                    float mp[MU], lp[MU], op[MU][4];
+#pragma unroll
+                    for (int u = 0; u < MU; ++u) {
+                        const int p = p0 + u * SL;
+                        const bool ok = p < nparts;
+                        mp[u] = ok ? load_partial(mlr + p) : -INFINITY;
+                        lp[u] = ok ? load_partial(esr + p) : 0.f;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) op[u][k] = ok ? load_partial(tor + (long)p * D + k) : 0.f;
+                    }
+#pragma unroll
+                    for (int u = 0; u < MU; ++u) {
+                        if (p0 + u * SL >= nparts) continue;
+                        if (mp[u] > m) {
+                            const float f = fast_exp2((m - mp[u]) * kLog2e);
+                            wsum *= f;
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) acc[k] *= f;
+                            m = mp[u];
+                        }
+                        const float w = fast_exp2((mp[u] - m) * kLog2e) * lp[u];
+                        wsum += w;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, op[u][k], acc[k]);
+                    }
+                }
+                float *f6 = fold + (sl * COLS + c) * 6;
+                f6[0] = m;
+                f6[1] = wsum;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) f6[2 + k] = acc[k];
+            }
+            __syncthreads();
+            for (int c = tid; c < COLS; c += T) {
+                const int h = c / (D / 4), d0 = 4 * (c % (D / 4));
+                float M = -INFINITY;
+#pragma unroll
+                for (int sl = 0; sl < SL; ++sl) M = fmaxf(M, fold[(sl * COLS + c) * 6]);
+                float ws = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < SL; ++sl) {
+                    const float *f6 = fold + (sl * COLS + c) * 6;
+                    const float f = f6[1] > 0.f ? fast_exp2((f6[0] - M) * kLog2e) : 0.f;
+                    ws = fmaf(f, f6[1], ws);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) a[k] = fmaf(f, f6[2 + k], a[k]);
+                }
+                const float inv = 1.f / ws;
+                u32x2 wv;
+                wv[0] = pack_bf16x2(a[0] * inv, a[1] * inv);
+                wv[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
+                *reinterpret_cast<u32x2 *>(prm.out + (row0 + h) * D + d0) = wv;
+            }
+            if (tid == 0)
+                __hip_atomic_store(prm.counters + (long)seq * prm.num_kv_heads + kvh, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    wg_sync();  // the next item of a persistent workgroup reuses `lds`
+}
+
+// One workgroup per (partition, kv head, sequence); workgroups whose partition
+// starts past the sequence end exit at once.
+template <int D, int G, int NW, int DEPTH, bool FP8>
+__global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams prm) {
+    using S = DecodeShape<D, G, NW>;
+    __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    const int seq = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
+    const int L = prm.seq_lens[seq];
+    const int P = prm.partition_size;
+    if ((P ? part * P : 0) >= L) {
+        if (P == 0) {  // empty sequence, single pass: zeros
+            uint16_t *o = prm.out + ((long)seq * prm.num_q_heads + kvh * G) * D;
+            for (int e = threadIdx.x; e < G * D; e += NW * 64) o[e] = 0;
+        }
+        return;
+    }
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const DecodeItem it = make_item<NW>(prm, seq, kvh, part, L, wave, threadIdx.x & 63);
+    u32x4 qb[D / 32], kbuf[DEPTH + 1][KvWords<D, FP8>::N], vbuf[DEPTH + 1][KvWords<D, FP8>::N];
+    decode_item<D, G, NW, DEPTH, false, FP8>(prm, it, it, false, false, qb, kbuf, vbuf, lds);
+}
+
+// Compact persistent split-KV: every workgroup first builds, in LDS, the
+// prefix over sequences of their item counts H_kv * ceil(L / P) (items are
+// ordered sequence, kv head, partition), then takes items blockIdx.x,
+// blockIdx.x + gridDim.x, ...  Only partitions that exist are ever visited, so
+// no workgroup is spent on the empty tail of an upper-bound grid.  Each item
+// issues the next one's query rows and first K/V tiles before its epilogue.
+constexpr int kCompactMaxSeqs = 1024;
+
+template <int D, int G, int NW, int DEPTH, bool FP8>
+__global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodeParams prm) {
+    using S = DecodeShape<D, G, NW>;
+    constexpr int T = NW * 64;
+    constexpr int PER = (kCompactMaxSeqs + T - 1) / T;
+    __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    __shared__ int pref[kCompactMaxSeqs + 1];
+    __shared__ int lens[kCompactMaxSeqs];
+    __shared__ int wtot[NW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nseq = prm.num_seqs, P = prm.partition_size, hkv = prm.num_kv_heads;
+
+    int cnt[PER];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid * PER + k;
+        int c = 0;
+        if (i < nseq) {
+            const int L = prm.seq_lens[i];
+            c = L > 0 ? hkv * ((L + P - 1) / P) : 0;
+            lens[i] = L;
+        }
+        cnt[k] = c;
+        local += c;
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid * PER + k;
+        run += cnt[k];
+        if (i < nseq) pref[i + 1] = run;
+    }
+    if (tid == 0) pref[0] = 0;
+    __syncthreads();
+
+    const int total = __builtin_amdgcn_readfirstlane(pref[nseq]);  // uniform loop bound
+    // item -> its description: (sequence, kv head, partition) is found as the
+    // largest s with pref[s] <= item, then the rest within the sequence
+    auto locate = [&](int item) {
+        int lo = 0, hi = nseq;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pref[mid] <= item) lo = mid; else hi = mid;
+        }
+        const int seq = __builtin_amdgcn_readfirstlane(lo);
+        const int np = (pref[seq + 1] - pref[seq]) / hkv;
+        const int rr = item - pref[seq];
+        const int kvh = __builtin_amdgcn_readfirstlane(rr / np);
+        const int part = __builtin_amdgcn_readfirstlane(rr % np);
+        return make_item<NW>(prm, seq, kvh, part, lens[seq], wave, lane);
+    };
+    int item = blockIdx.x;
+    if (item >= total) return;
+    DecodeItem it = locate(item);
+    // Settle the first item's block-id load here: the wait the compiler would
+    // otherwise place at the top of the item loop (where it would also drain
+    // the prefetched loads of every later item) becomes a no-op.
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 qb[D / 32], kbuf[DEPTH + 1][KvWords<D, FP8>::N], vbuf[DEPTH + 1][KvWords<D, FP8>::N];
+    bool primed = false;
+    for (;;) {
+        // the next item's block ids are fetched while this one streams
+        const int next = item + gridDim.x;
+        const bool has_next = next < total;
+        const DecodeItem nx = has_next ? locate(next) : it;
+        decode_item<D, G, NW, DEPTH, true, FP8>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
+        if (!has_next) break;
+        item = next;
+        it = nx;
+        primed = true;
+    }
+}
+
+// Cross-partition merge (the BI-V100 page's combine rule): one workgroup per
+// (64-dim chunk, query head, sequence).  Its 16 slots of 16 lanes (4 dims per
+// lane) take partitions round-robin, 4 at a time, each slot keeping a running
+// max so that a single pass suffices; the slots are then folded in LDS in a
+// fixed order (deterministic).
+constexpr int kReduceChunk = 64;   // dims per workgroup
+constexpr int kReduceUnroll = 4;   // partitions in flight per slot
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
+    const float *__restrict__ max_logits, const float *__restrict__ exp_sums,
+    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens, int num_q_heads,
+    int head_dim, int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
+    constexpr int LPP = kReduceChunk / 4;  // lanes per partition row
+    constexpr int SLOTS = NW * 64 / LPP;
+    __shared__ __attribute__((aligned(16))) float red[SLOTS * kReduceChunk];
+    __shared__ float sm[SLOTS], sw[SLOTS];
+
+    const int chunk = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
+    const int tid = threadIdx.x;
+    const long row = (long)seq * num_q_heads + h;
+    const float *mlr = max_logits + row * max_num_partitions;
+    const float *esr = exp_sums + row * max_num_partitions;
+    const int slot = tid / LPP, dl = tid % LPP;
+    const float *base = tmp_out + row * (long)max_num_partitions * head_dim + chunk * kReduceChunk + dl * 4;
+    // When the partial buffers hold at most one record per slot, the first
+    // round is loaded before the sequence length is known (records past the
+    // sequence's partitions are discarded by selection, never used in
+    // arithmetic), which takes one dependent memory round trip off the
+    // kernel.  With more partition slots than that, most of them are unused
+    // for short sequences, so the length comes first and only existing
+    // partitions are read.
+    const bool speculate = max_num_partitions <= SLOTS;
+    int n = 0;
+    if (!speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    const int first_bound = speculate ? max_num_partitions : n;
+    float mv[kReduceUnroll], ev[kReduceUnroll];
+    f32x4 v[kReduceUnroll];
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+        const int p = slot + u * SLOTS;
+        const bool in = p < first_bound;
+        mv[u] = in ? mlr[p] : -INFINITY;
+        ev[u] = in ? esr[p] : 0.f;
+        v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    uint16_t *o = out + row * head_dim + chunk * kReduceChunk;
+    if (n == 0) {
+        for (int d = tid; d < kReduceChunk; d += NW * 64) o[d] = 0;
+        return;
+    }
+
+    float m = -INFINITY, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = slot;; p0 += SLOTS * kReduceUnroll) {
+#pragma unroll
+        for (int u = 0; u < kReduceUnroll; ++u) {
+            if (p0 + u * SLOTS >= n) continue;
+            if (mv[u] > m) {  // rescale what was accumulated to the new max
+                const float f = fast_exp2((m - mv[u]) * kLog2e);
+                acc *= f;
+                wsum *= f;
+                m = mv[u];
+            }
+            const float w = fast_exp2((mv[u] - m) * kLog2e) * ev[u];
+            acc[0] = fmaf(w, v[u][0], acc[0]);
+            acc[1] = fmaf(w, v[u][1], acc[1]);
+            acc[2] = fmaf(w, v[u][2], acc[2]);
+            acc[3] = fmaf(w, v[u][3], acc[3]);
+            wsum += w;
+        }
+        const int q0 = p0 + SLOTS * kReduceUnroll;
+        if (q0 >= n) break;
+#pragma unroll
+        for (int u = 0; u < kReduceUnroll; ++u) {
+            const int p = q0 + u * SLOTS;
+            const bool ok = p < n;
+            mv[u] = ok ? mlr[p] : -INFINITY;
+            ev[u] = ok ? esr[p] : 0.f;
+            v[u] = ok ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    *reinterpret_cast<f32x4 *>(red + slot * kReduceChunk + dl * 4) = acc;
+    if (dl == 0) {
+        sm[slot] = m;
+        sw[slot] = wsum;
+    }
+    __syncthreads();
+    for (int d = tid; d < kReduceChunk; d += NW * 64) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) M = fmaxf(M, sm[sl]);
+        float a = 0.f, ws = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) {
+            const float f = sw[sl] > 0.f ? fast_exp2((sm[sl] - M) * kLog2e) : 0.f;
+            a = fmaf(f, red[sl * kReduceChunk + d], a);
+            ws = fmaf(f, sw[sl], ws);
+        }
+        o[d] = (uint16_t)f32_to_bf16_bits(a / ws);
+    }
+}
+
+// Cross-partition merge for partial buffers with few partition slots (a
+// batch of many sequences with a handful of partitions each): one wave per
+// (sequence, query head).  The wave's lanes form R = 256 / D rows of D / 4
+// lanes (4 dims per lane); the rows take partitions round-robin, 4 at a time
+// with every load issued before any is used, each row keeping a running max.
+// The rows are then folded with lane swaps (rows 16 and 32 lanes apart) using
+// only symmetric operations, so every lane of a fold holds the same result.
+// When every slot fits in the first round, the records are loaded before the
+// sequence length is known (records past the sequence's partitions are
+// discarded by selection, never used in arithmetic).
+constexpr int kWaveReduceUnroll = 4;
+constexpr int kWaveReduceMaxRounds = 8;  // slots per row beyond this use paged_reduce_kernel
+
+template <int D>
+__global__ __launch_bounds__(256) void paged_reduce_wave_kernel(
+    const float *__restrict__ max_logits, const float *__restrict__ exp_sums,
+    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens, int num_seqs,
+    int num_q_heads, int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
+    constexpr int LPR = D / 4;   // lanes per row
+    constexpr int R = 64 / LPR;  // rows per wave
+    constexpr int U = kWaveReduceUnroll;
+    const int lane = threadIdx.x & 63;
+    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // sequence * H_q + head
+    if (pair >= (long)num_seqs * num_q_heads) return;
+    const int seq = (int)(pair / num_q_heads);
+    const int r = lane / LPR, d0 = 4 * (lane % LPR);
+    const float *mlr = max_logits + pair * max_num_partitions;
+    const float *esr = exp_sums + pair * max_num_partitions;
+    const float *base = tmp_out + pair * (long)max_num_partitions * D + d0;
+    const bool speculate = max_num_partitions <= R * U;
+    int n = 0;
+    if (!speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    const int first_bound = speculate ? max_num_partitions : n;
+    float mv[U], ev[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int p = r + u * R;
+        const bool in = p < first_bound;
+        mv[u] = in ? mlr[p] : -INFINITY;
+        ev[u] = in ? esr[p] : 0.f;
+        v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (speculate) {
+        const int L = seq_lens[seq];
+        n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+    }
+    uint16_t *o = out + pair * D + d0;
+    if (n == 0) {
+        if (r == 0) *reinterpret_cast<u32x2 *>(o) = u32x2{0u, 0u};
+        return;
+    }
+    float m = -INFINITY, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = r;; p0 += R * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (p0 + u * R >= n) continue;
+            if (mv[u] > m) {  // rescale what was accumulated to the new max
+                const float f = fast_exp2((m - mv[u]) * kLog2e);
+                acc *= f;
+                wsum *= f;
+                m = mv[u];
+            }
+            const float w = fast_exp2((mv[u] - m) * kLog2e) * ev[u];
+            acc[0] = fmaf(w, v[u][0], acc[0]);
+            acc[1] = fmaf(w, v[u][1], acc[1]);
+            acc[2] = fmaf(w, v[u][2], acc[2]);
+            acc[3] = fmaf(w, v[u][3], acc[3]);
+            wsum += w;
+        }
+        const int q0 = p0 + R * U;
+        if (__all(q0 >= n)) break;  // wave-uniform exit; rows past n load nothing below
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = q0 + u * R;
+            const bool ok = p < n;
+            mv[u] = ok ? mlr[p] : -INFINITY;
+            ev[u] = ok ? esr[p] : 0.f;
+            v[u] = ok ? *reinterpret_cast<const f32x4 *>(base + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // fold the rows: rescale each to the common max, then sum
+    auto fold = [&](auto max_x, auto sum_x) {
+        const float M = max_x(m);
+        const float f = wsum > 0.f ? fast_exp2((m - M) * kLog2e) : 0.f;
+        wsum = sum_x(f * wsum);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = sum_x(f * acc[k]);
+        m = M;
+    };
+    if constexpr (R >= 4) fold([](float x) { return max_xor16(x); }, [](float x) { return sum_xor16(x); });
+    if constexpr (R >= 2) fold([](float x) { return max_xor32(x); }, [](float x) { return sum_xor32(x); });
+    if (r == 0) {
+        const float inv = 1.f / wsum;
+        *reinterpret_cast<u32x2 *>(o) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                             pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch of the partition kernels (instantiated per cache type by
+// decode.hip and decode_fp8.hip)
+// ---------------------------------------------------------------------------
+namespace launch_detail {
+// Waves per decode workgroup and register prefetch depth (tiles in flight per
+// wave while one is consumed; deeper costs D/4 VGPRs per tile).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;
+#ifdef PA_DECODE_DEPTH
+constexpr int decode_depth(int) { return PA_DECODE_DEPTH; }
+#else
+constexpr int decode_depth(int) { return 1; }
+#endif
+#ifndef PA_DECODE_PERSIST_PER_CU
+#define PA_DECODE_PERSIST_PER_CU 0   // 0 = as many workgroups per CU as fit
+#endif
+
+inline int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int D, int G, bool FP8>
+hipError_t launch_decode_dg(const DecodeArgs &a) {
+    constexpr int DEPTH = decode_depth(D);
+    DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
+                     a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2,
+                     a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
+                     a.tmp_out, a.counters, a.k_scales, a.v_scales};
+    dim3 block(kDecodeWaves * 64);
+    if (a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock && a.num_seqs <= kCompactMaxSeqs) {
+        static int per_cu = 0;  // resident workgroups per CU for this instantiation
+        if (per_cu == 0) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8>, block.x, 0) != hipSuccess || n <= 0)
+                n = 1;
+            per_cu = PA_DECODE_PERSIST_PER_CU > 0 ? PA_DECODE_PERSIST_PER_CU : n;
+        }
+        const long upper = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
+        const long cap = (long)cu_count() * per_cu;
+        dim3 grid((unsigned)(upper < cap ? upper : cap));
+        hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8>), grid, block, 0,
+                           a.stream, prm);
+    } else {
+        dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+        hipLaunchKernelGGL((paged_decode_grid_kernel<D, G, kDecodeWaves, DEPTH, FP8>), grid, block, 0,
+                           a.stream, prm);
+    }
+    return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_decode_d(const DecodeArgs &a, int G) {
+    switch (G) {
+        case 1: return launch_decode_dg<D, 1, FP8>(a);
+        case 2: return launch_decode_dg<D, 2, FP8>(a);
+        case 3: return launch_decode_dg<D, 3, FP8>(a);
+        case 4: return launch_decode_dg<D, 4, FP8>(a);
+        case 5: return launch_decode_dg<D, 5, FP8>(a);
+        case 6: return launch_decode_dg<D, 6, FP8>(a);
+        case 7: return launch_decode_dg<D, 7, FP8>(a);
+        case 8: return launch_decode_dg<D, 8, FP8>(a);
+        case 9: return launch_decode_dg<D, 9, FP8>(a);
+        case 10: return launch_decode_dg<D, 10, FP8>(a);
+        case 11: return launch_decode_dg<D, 11, FP8>(a);
+        case 12: return launch_decode_dg<D, 12, FP8>(a);
+        case 13: return launch_decode_dg<D, 13, FP8>(a);
+        case 14: return launch_decode_dg<D, 14, FP8>(a);
+        case 15: return launch_decode_dg<D, 15, FP8>(a);
+        case 16: return launch_decode_dg<D, 16, FP8>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Decode launch for a bf16 (FP8 false) or FP8 cache.
+template <bool FP8>
+hipError_t launch_decode_t(const DecodeArgs &a) {
+    const int G = a.num_q_heads / a.num_kv_heads;
+    switch (a.head_dim) {
+        case 64: return launch_decode_d<64, FP8>(a, G);
+        case 128: return launch_decode_d<128, FP8>(a, G);
+        case 256: return launch_decode_d<256, FP8>(a, G);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace launch_detail
+
+}  // namespace pa

@@ -22,6 +22,9 @@ struct DecodeArgs {
     uint16_t *out;
     float *max_logits, *exp_sums, *tmp_out;
     int32_t *counters;         // fused merge counters, or null
+    // FP8 cache: k_cache / v_cache hold E4M3 codes and these the per-position
+    // dequant scales [num_blocks, H_kv, block_size]; null for a bf16 cache
+    const float *k_scales = nullptr, *v_scales = nullptr;
     hipStream_t stream;
 };
 
@@ -59,8 +62,21 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+// KV append (bf16 copy or FP8 quantization) of new rows into their cache slots.
+struct AppendArgs {
+    const void *k_new, *v_new;          // bf16 [num_tokens, H_kv, D]
+    const int32_t *block_tables, *seq_lens, *cu_seqlens;
+    int num_seqs, max_new_tokens, num_kv_heads, head_dim, max_blocks_per_seq;
+    void *k_cache, *v_cache;            // bf16 values or E4M3 codes [num_blocks, H_kv, 16, D]
+    float *k_scales, *v_scales;         // FP8: dequant scales [num_blocks, H_kv, 16]
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_decode_fp8(const DecodeArgs &a);
 hipError_t launch_reduce(const ReduceArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
+hipError_t launch_kv_append(const AppendArgs &a);
+hipError_t launch_kv_append_fp8(const AppendArgs &a);
 
 }  // namespace pa

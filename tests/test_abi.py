@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
         "paged_attn_prefill_chunk_size", "paged_attn_prefill_workspace_size",
         "paged_attn_num_partitions", "paged_attn_choose_partition_size",
-        "paged_attn_prefill_tile_map", "paged_attn_status_string"} | (
+        "paged_attn_prefill_tile_map", "paged_attn_status_string", "paged_attn_decode_fp8",
+        "paged_attn_kv_append", "paged_attn_kv_append_fp8"} | (
         set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
     for name in names:
         assert hasattr(lib, name), name
@@ -251,3 +252,63 @@ def test_prefill_chunk_size_heuristic(lib):
     assert pa.paged_attn_prefill_chunk_size(0, 10, 32, 8, 100, 16) == 0
     # more than 128 query heads: single pass
     assert pa.paged_attn_prefill_chunk_size(2, 100, 256, 16, 1000, 16) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ks=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(vs=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(q=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(ks=FAKE + 4), pa.PA_ERR_ALIGNMENT),
+    (dict(vs=FAKE + 8), pa.PA_ERR_ALIGNMENT),
+    (dict(k=FAKE + 1), pa.PA_ERR_ALIGNMENT),
+    (dict(P=24, NP=5), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), pa.PA_ERR_BAD_VALUE),
+    (dict(S=0), pa.PA_OK),
+])
+def test_decode_fp8_validation(lib, over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=4, Hkv=1, D=64,
+             bs=16, nb=16, mbps=7, scale=0.125, P=0, out=FAKE, ml=FAKE, es=FAKE, to=FAKE, NP=1)
+    a.update(over)
+    st = lib.paged_attn_decode_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["sl"], a["S"],
+                                   a["Hq"], a["Hkv"], a["D"], a["bs"], a["nb"], a["mbps"], a["scale"],
+                                   a["P"], a["out"], a["ml"], a["es"], a["to"], a["NP"], None)
+    assert st == status
+
+
+def append_call(lib, fp8, **over):
+    a = dict(kn=FAKE, vn=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, S=3, T=40, maxn=20, Hkv=8, D=128, bs=16,
+             nb=64, mbps=9, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE)
+    a.update(over)
+    common = (a["kn"], a["vn"], a["bt"], a["sl"], a["cu"], a["S"], a["T"], a["maxn"], a["Hkv"],
+              a["D"], a["bs"], a["nb"], a["mbps"], a["kc"], a["vc"])
+    if fp8:
+        return lib.paged_attn_kv_append_fp8(*common, a["ks"], a["vs"], None)
+    return lib.paged_attn_kv_append(*common, None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("over,status", [
+    (dict(kn=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(cu=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(vc=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(S=-1), pa.PA_ERR_BAD_SHAPE),
+    (dict(T=-1), pa.PA_ERR_BAD_SHAPE),
+    (dict(Hkv=0), pa.PA_ERR_BAD_SHAPE),
+    (dict(maxn=41), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=80), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(kn=FAKE + 2), pa.PA_ERR_ALIGNMENT),
+    (dict(vc=FAKE + 8), pa.PA_ERR_ALIGNMENT),
+    (dict(S=0), pa.PA_OK),
+    (dict(T=0, maxn=0), pa.PA_OK),
+])
+def test_kv_append_validation(lib, fp8, over, status):
+    assert append_call(lib, fp8, **over) == status
+
+
+def test_kv_append_fp8_needs_scales(lib):
+    assert append_call(lib, True, ks=NULL) == pa.PA_ERR_NULL_POINTER
+    assert append_call(lib, True, vs=FAKE + 4) == pa.PA_ERR_ALIGNMENT
+    # the bf16 form takes no scales: its validation never looks at them
+    assert append_call(lib, False, maxn=41, ks=NULL, vs=NULL) == pa.PA_ERR_BAD_SHAPE
