@@ -40,7 +40,8 @@ METRIC = "KV tokens/sec and achieved HBM GB/s (% of peak), paged GQA decode, 1 M
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_34_amd", "csrc", "decode.hip")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_34_amd", "csrc", "decode_kernels.h")
+APPEND_SOURCE = os.path.join(ROOT, "paged_kv_cache_34_amd", "csrc", "kvcache.hip")
 PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_34_amd", "csrc", "prefill.hip")
 
 
@@ -110,6 +111,33 @@ def to_device(case):
     return d
 
 
+def to_fp8_cache(pa, case, d):
+    """Quantize a device copy of a bf16 case into an FP8 cache with the
+    library's own append kernel: every token of every sequence is appended
+    (its rows gathered from the bf16 pool through the block table)."""
+    import numpy as np
+    import torch
+    lens = torch.from_numpy(case.seq_lens.astype(np.int64)).cuda()
+    S, bs = case.num_seqs, case.block_size
+    seq_of = torch.repeat_interleave(torch.arange(S, device="cuda"), lens)
+    starts = torch.cumsum(lens, 0) - lens
+    tok = torch.arange(int(lens.sum()), device="cuda") - starts[seq_of]
+    phys = d["bt"][seq_of, tok // bs].long()
+    k_rows = d["k"][phys, :, tok % bs, :].contiguous()
+    v_rows = d["v"][phys, :, tok % bs, :].contiguous()
+    cu = torch.zeros(S + 1, dtype=torch.int32, device="cuda")
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    shape = tuple(d["k"].shape)
+    kc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+    vs = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+    pa.paged_attn_kv_append_fp8(k_rows, v_rows, d["bt"], d["sl"], cu, int(case.seq_lens.max()),
+                                kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    return dict(q=d["q"], k=kc, v=vc, ks=ks, vs=vs, bt=d["bt"], sl=d["sl"])
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on host cores, bounded sample
 # ---------------------------------------------------------------------------
@@ -165,12 +193,28 @@ def run_decode(args, pa):
         P = pa.paged_attn_choose_partition_size(c0.num_seqs, c0.num_kv_heads, int(c0.seq_lens.max()),
                                                 c0.kv_tokens)
     devs = [to_device(c) for c in cases]
+    fp8 = args.kv_dtype == "fp8"
+    if fp8:
+        t0 = time.perf_counter()
+        devs = [to_fp8_cache(pa, c, d) for c, d in zip(cases, devs)]
+        log(f"quantized {copies} pool copies to FP8 on the GPU in {time.perf_counter() - t0:.1f} s")
     npart = pa.paged_attn_num_partitions(c0.max_blocks_per_seq, c0.block_size, P) if P else 1
     ws = pa.DecodeWorkspace(c0.num_seqs, c0.num_q_heads, c0.head_dim, npart, "cuda",
                             num_kv_heads=c0.num_kv_heads) if P else None
     # the merge is a separate kernel unless --merge fused asks for the
     # last-workgroup merge inside the partition kernel
     fused = bool(P) and args.merge == "fused"
+    if fused and fp8:
+        raise SystemExit("--merge fused is not available with --kv-dtype fp8")
+
+    def decode_call(d, out_or_none):
+        kw = dict(max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
+                  max_num_partitions=npart) if P else dict(out=out_or_none)
+        if fp8:
+            pa.paged_attn_decode_fp8(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["bt"], d["sl"], scale,
+                                     P, stream=stream, **kw)
+        else:
+            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P, stream=stream, **kw)
     out = torch.empty_like(devs[0]["q"])
     scale = float(c0.scale)
     stream = torch.cuda.current_stream()
@@ -182,13 +226,7 @@ def run_decode(args, pa):
                                        ws.max_logits, ws.exp_sums, ws.tmp_out, ws.counters,
                                        stream=stream)
             return
-        if P:
-            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
-                                 max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
-                                 max_num_partitions=npart, stream=stream)
-        else:
-            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, 0, out=out,
-                                 stream=stream)
+        decode_call(d, out)
         if P:
             pa.paged_attn_decode_reduce(ws.max_logits, ws.exp_sums, ws.tmp_out, d["sl"], P, out,
                                         stream=stream)
@@ -211,13 +249,7 @@ def run_decode(args, pa):
         if fused:
             step(i)
             return
-        if P:
-            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
-                                 max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
-                                 max_num_partitions=npart, stream=stream)
-        else:
-            pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, 0, out=out,
-                                 stream=stream)
+        decode_call(d, out)
 
     torch.cuda.synchronize()
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -231,11 +263,15 @@ def run_decode(args, pa):
     step(0)
     torch.cuda.synchronize()
 
-    kv_bytes = c0.kv_bytes
     tokens = c0.kv_tokens
+    # algorithmic bytes per KV token: K and V of every kv head -- bf16 values,
+    # or E4M3 codes plus one fp32 scale per (position, kv head) each
+    bytes_per_token = c0.num_kv_heads * 2 * (c0.head_dim + 4 if fp8 else 2 * c0.head_dim)
+    kv_bytes = tokens * bytes_per_token
     step_gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     kern_gbps = kv_bytes / (ms_kernel * 1e-3) / 1e9
-    traffic = counter_traffic("decode", DECODE_SOURCE, args.workload)
+    traffic = counter_traffic("decode_fp8" if fp8 else "decode", DECODE_SOURCE,
+                              args.workload)
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -247,10 +283,11 @@ def run_decode(args, pa):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 kv, bf16 q" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": args.workload + ("_fp8" if fp8 else ""),
+            "kv_cache": "fp8 e4m3 + per-position fp32 scales" if fp8 else "bf16",
             "num_seqs": c0.num_seqs,
             "num_q_heads": c0.num_q_heads,
             "num_kv_heads": c0.num_kv_heads,
@@ -268,7 +305,8 @@ def run_decode(args, pa):
         "accumulate": "fp32",
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_compact_kernel (fused merge)" if fused else "paged_decode_compact_kernel",
+            "kernel": ("paged_decode_compact_kernel (fused merge)" if fused else "paged_decode_compact_kernel")
+                      + (" <FP8>" if fp8 else ""),
             "achieved": kern_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -346,6 +384,66 @@ def run_prefill(args, pa):
     return result, case
 
 
+def run_append(args, pa):
+    """KV append of the ragged prefill batch's new rows (its 16 sequences'
+    U[1, 256] new tokens after U[0, 8192] cached ones): bf16 copy or FP8
+    quantize-and-write into the paged cache, HBM-bound."""
+    import numpy as np
+    import torch
+    import workloads
+    case = workloads.ragged_prefill()
+    d = to_device(case)
+    fp8 = args.kv_dtype == "fp8"
+    total, hkv, D = case.total_q, case.num_kv_heads, case.head_dim
+    g = torch.Generator(device="cuda").manual_seed(case.seed)
+    k_new = torch.randn((total, hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    v_new = torch.randn((total, hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    shape = tuple(d["k"].shape)
+    if fp8:
+        kc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+        vc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+        vs = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    maxn = case.max_q_len
+
+    def step():
+        if fp8:
+            pa.paged_attn_kv_append_fp8(k_new, v_new, d["bt"], d["sl"], d["cu"], maxn, kc, vc, ks, vs,
+                                        stream=stream)
+        else:
+            pa.paged_attn_kv_append(k_new, v_new, d["bt"], d["sl"], d["cu"], maxn, d["k"], d["v"],
+                                    stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    # algorithmic bytes: the new K and V rows read (bf16) and written (bf16, or
+    # E4M3 codes plus one fp32 scale per row)
+    rows = total * hkv * 2
+    nbytes = rows * D * 2 + rows * (D + 4 if fp8 else 2 * D)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "KV append bandwidth, paged KV cache write, 1 MI355X",
+        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 -> fp8-e4m3" if fp8 else "bf16", "data": "synthetic",
+        "config": {"workload": "kv_append" + ("_fp8" if fp8 else ""), "num_seqs": case.num_seqs,
+                   "new_tokens": total, "num_kv_heads": hkv, "head_dim": D},
+        "roofline": {"bound": "hbm", "kernel": "paged_kv_append_fp8_kernel" if fp8 else "paged_kv_append_kernel",
+                     "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+                     "traffic": counter_traffic("append_fp8" if fp8 else "append", APPEND_SOURCE, "kv_append"),
+                     "kernel_ms": ms, "algorithmic_bytes_per_launch": nbytes},
+    }, None
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -365,7 +463,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_split_decode", "large_ragged_decode",
-                             "ragged_prefill", "tiny_decode"])
+                             "ragged_prefill", "tiny_decode", "kv_append"])
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="decode workloads and kv_append: bf16 cache, or FP8 (E4M3 codes with "
+                         "per-position scales) quantized on the GPU by the library's append kernel")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--copies", type=int, default=None,
                     help="independent KV pool copies rotated across steps (default 3, or 2 for >1 GB pools)")
@@ -396,9 +497,11 @@ def main():
     pa = ensure_library()
     if args.workload == "ragged_prefill":
         result, case = run_prefill(args, pa)
+    elif args.workload == "kv_append":
+        result, case = run_append(args, pa)
     else:
         result, case = run_decode(args, pa)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and case is not None and args.kv_dtype == "bf16":
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, args.workload == "ragged_prefill")
     else:
