@@ -924,11 +924,13 @@ namespace launch_detail {
 #define PA_DECODE_WAVES 4
 #endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;
-#ifdef PA_DECODE_DEPTH
-constexpr int decode_depth(int) { return PA_DECODE_DEPTH; }
-#else
-constexpr int decode_depth(int) { return 1; }
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 1
 #endif
+#ifndef PA_DECODE_DEPTH_FP8
+#define PA_DECODE_DEPTH_FP8 1
+#endif
+constexpr int decode_depth(int, bool fp8) { return fp8 ? PA_DECODE_DEPTH_FP8 : PA_DECODE_DEPTH; }
 #ifndef PA_DECODE_PERSIST_PER_CU
 #define PA_DECODE_PERSIST_PER_CU 0   // 0 = as many workgroups per CU as fit
 #endif
@@ -947,7 +949,7 @@ inline int cu_count() {
 
 template <int D, int G, bool FP8>
 hipError_t launch_decode_dg(const DecodeArgs &a) {
-    constexpr int DEPTH = decode_depth(D);
+    constexpr int DEPTH = decode_depth(D, FP8);
     DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
                      a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2,
                      a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,

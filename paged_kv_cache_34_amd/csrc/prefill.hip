@@ -540,53 +540,82 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
 }
 
 // Merge of the split-KV partial records (the BI-V100 page's combine rule):
-// one workgroup per query row; rows whose keys all lie in the first chunk
-// were written by the prefill kernel and are skipped.  The chunk weights
-// w_j = 2^(m_j - M) l_j / sum_j' 2^(m_j' - M) l_j' of every head go to LDS
-// first; then each thread forms 4 consecutive output dims of one head from
-// 16-byte loads of the chunk outputs, chunks in a fixed order.
+// one workgroup per (new row, sequence); rows whose keys all lie in the first
+// chunk were written by the prefill kernel and are skipped.  The chunk maxima
+// and exp-sums of every head are staged in LDS with one round of independent
+// loads; each head's maximum M and sum S = sum_j 2^(m_j - M) l_j come from
+// LDS; the weights w_j = 2^(m_j - M) l_j / S replace the staged maxima; then
+// each thread forms 4 consecutive output dims of one head from 16-byte loads
+// of the chunk outputs, chunks in a fixed order.  Rows with more chunks than
+// one LDS pass holds take several passes (the running sum is parked in chunk
+// 0's record between them).
 constexpr int kMergeThreads = 256;
 constexpr int kMergeMaxHeads = kPfMaxHeads;  // query heads per row held in LDS
-constexpr int kMergeMaxSplits = 64;   // chunks per row held in LDS (more: a second pass)
+constexpr int kMergeSplits = 32;             // chunks per row held in LDS per pass
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfParams prm) {
-    __shared__ float wts[kMergeMaxHeads * kMergeMaxSplits];
-    const int row = blockIdx.x;
-    int lo = 0, hi = prm.num_seqs;  // the sequence owning the row: last s with cu[s] <= row
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (prm.cu_seqlens[mid] <= row) lo = mid; else hi = mid;
-    }
-    const int q0 = prm.cu_seqlens[lo];
-    const int n = prm.cu_seqlens[lo + 1] - q0;
-    const int visible = prm.seq_lens[lo] - n + (row - q0) + 1;
+    __shared__ float sm[kMergeMaxHeads * kMergeSplits];  // chunk maxima, then weights
+    __shared__ float sl[kMergeMaxHeads * kMergeSplits];  // chunk exp-sums
+    __shared__ float hmax[kMergeMaxHeads], hsum[kMergeMaxHeads];
+    constexpr int T = kMergeThreads, SP = kMergeSplits;
+    const int s = blockIdx.y, jrow = blockIdx.x;  // sequence, new row within it
+    const int q0 = prm.cu_seqlens[s];
+    const int n = prm.cu_seqlens[s + 1] - q0;
+    if (jrow >= n) return;
+    const int visible = prm.seq_lens[s] - n + jrow + 1;
     const int ns = (visible + prm.chunk - 1) / prm.chunk;
     if (ns <= 1) return;
-    const int hq = prm.num_q_heads;
+    const int row = q0 + jrow, hq = prm.num_q_heads;
     const long rec_row = (long)row * hq * prm.max_splits;
-    for (int j0 = 0; j0 < ns; j0 += kMergeMaxSplits) {
-        // weights of chunks j0 .. j0+nj-1 relative to the max and sum over all ns
-        const int nj = min(kMergeMaxSplits, ns - j0);
-        for (int h = threadIdx.x; h < hq; h += kMergeThreads) {
-            const float *mh = prm.ws_m + rec_row + (long)h * prm.max_splits;
-            const float *lh = prm.ws_l + rec_row + (long)h * prm.max_splits;
-            float M = -INFINITY;
-            for (int j = 0; j < ns; ++j) M = fmaxf(M, mh[j]);
-            float wsum = 0.f;
-            for (int j = 0; j < ns; ++j) wsum += fast_exp2(mh[j] - M) * lh[j];
-            const float inv = 1.f / wsum;
-            for (int j = 0; j < nj; ++j) wts[h * kMergeMaxSplits + j] = fast_exp2(mh[j0 + j] - M) * lh[j0 + j] * inv;
+    auto stage = [&](int j0, int nj) {
+        for (int e = threadIdx.x; e < hq * nj; e += T) {
+            const int h = e / nj, j = e - h * nj;
+            const long r = rec_row + (long)h * prm.max_splits + j0 + j;
+            sm[h * SP + j] = prm.ws_m[r];
+            sl[h * SP + j] = prm.ws_l[r];
+        }
+    };
+    // per-head maximum and exp-sum over all chunks (online across passes)
+    for (int j0 = 0; j0 < ns; j0 += SP) {
+        const int nj = min(SP, ns - j0);
+        if (j0 > 0) __syncthreads();
+        stage(j0, nj);
+        __syncthreads();
+        for (int h = threadIdx.x; h < hq; h += T) {
+            float M = j0 ? hmax[h] : -INFINITY, S = j0 ? hsum[h] : 0.f;
+            for (int j = 0; j < nj; ++j) {
+                const float mj = sm[h * SP + j];
+                if (mj > M) {
+                    S *= fast_exp2(M - mj);
+                    M = mj;
+                }
+                S += fast_exp2(mj - M) * sl[h * SP + j];
+            }
+            hmax[h] = M;
+            hsum[h] = S;
+        }
+    }
+    // weights and the weighted sum, pass by pass
+    for (int j0 = 0; j0 < ns; j0 += SP) {
+        const int nj = min(SP, ns - j0);
+        __syncthreads();
+        if (ns > SP) {  // (a single pass still holds its records in LDS)
+            stage(j0, nj);
+            __syncthreads();
+        }
+        for (int e = threadIdx.x; e < hq * nj; e += T) {
+            const int h = e / nj, j = e - h * nj;
+            sm[h * SP + j] = fast_exp2(sm[h * SP + j] - hmax[h]) * sl[h * SP + j] / hsum[h];
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < hq * (D / 4); e += kMergeThreads) {
+        for (int e = threadIdx.x; e < hq * (D / 4); e += T) {
             const int h = e / (D / 4), d0 = (e % (D / 4)) * 4;
-            const float *w = wts + h * kMergeMaxSplits;
+            const float *w = sm + h * SP;
             const float *o = prm.ws_o + (rec_row + (long)h * prm.max_splits + j0) * D + d0;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (j0 > 0) {  // continue the first pass's sum, kept in the output tile
-                const float *prev = reinterpret_cast<const float *>(prm.ws_o) +
-                                    (rec_row + (long)h * prm.max_splits) * D + d0;
+            if (j0 > 0) {  // continue the earlier passes' sum, parked in chunk 0's record
+                const float *prev = prm.ws_o + (rec_row + (long)h * prm.max_splits) * D + d0;
                 acc = *reinterpret_cast<const f32x4 *>(prev);
             }
             int j = 0;
@@ -602,7 +631,6 @@ __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfPa
             }
             for (; j < nj; ++j) acc += w[j] * *reinterpret_cast<const f32x4 *>(o + (long)j * D);
             if (j0 + nj < ns) {
-                // more chunks follow: park the running sum in chunk 0's record
                 float *first = prm.ws_o + (rec_row + (long)h * prm.max_splits) * D + d0;
                 *reinterpret_cast<f32x4 *>(first) = acc;
             } else {
@@ -613,7 +641,6 @@ __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfPa
                 *reinterpret_cast<u32x2 *>(orow) = wv;
             }
         }
-        __syncthreads();
     }
 }
 
@@ -650,7 +677,8 @@ hipError_t launch_prefill_dg(const PrefillArgs &a) {
                            a.stream, prm);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.total_q), dim3(kMergeThreads), 0, a.stream, prm);
+        hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.max_q_len, a.num_seqs), dim3(kMergeThreads), 0,
+                           a.stream, prm);
         return hipGetLastError();
     }
     dim3 grid((a.max_q_len + R - 1) / R, a.num_kv_heads, a.num_seqs);
