@@ -25,6 +25,9 @@ Definitions followed (details in the C source):
                  page, "Stage D: FP8 Paged KV Gather" and "FP8 KV
                  Quantize/Dequant"): quantize_fp8, fp8_dequant, kv_append_fp8,
                  and decode / partials over the dequantized (fp64) cache.
+  xpacked     -- the BI-V100 page's cache layouts (section 3 "Paged K/V
+                 Gather"): K [num_blocks, H_kv, D/8, bs, 8], V [num_blocks,
+                 H_kv, D, bs]; decode, partials and append over them.
 """
 from __future__ import annotations
 
@@ -47,10 +50,11 @@ _c_int = ctypes.c_int
 
 def compile_library(out_path: str = LIBRARY, mutant: int = 0) -> str:
     """Compile the oracle with gcc (portable flags: it runs on other hosts too)."""
+    tmp = f"{out_path}.tmp{os.getpid()}"  # one per process: parallel builds do not collide
     cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99",
-           f"-DORACLE_MUTANT={int(mutant)}", SOURCE, "-o", out_path + ".tmp", "-lm"]
+           f"-DORACLE_MUTANT={int(mutant)}", SOURCE, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(out_path + ".tmp", out_path)
+    os.replace(tmp, out_path)
     return out_path
 
 
@@ -80,6 +84,9 @@ class Oracle:
         lib.oracle_decode_partials_f64kv.argtypes = [_u16p, _f64p, _f64p, _i32p, _i32p] + [_c_int] * 6 + [
             ctypes.c_float, _c_int, _c_int, _f64p, _f64p, _f64p]
         lib.oracle_kv_append.argtypes = [_u16p, _u16p, _i32p, _i32p, _i32p] + [_c_int] * 5 + [_u16p, _u16p]
+        lib.oracle_kv_append_xpacked.argtypes = lib.oracle_kv_append.argtypes
+        lib.oracle_decode_xpacked.argtypes = lib.oracle_decode.argtypes
+        lib.oracle_decode_partials_xpacked.argtypes = lib.oracle_decode_partials.argtypes
         lib.oracle_kv_append_fp8.argtypes = ([_u16p, _u16p, _i32p, _i32p, _i32p] + [_c_int] * 5 +
                                              [_u8p, _u8p, _f32p, _f32p])
         lib.oracle_quantize_fp8.argtypes = [_u16p, ctypes.c_long, _c_int, _u8p, _f32p]
@@ -89,7 +96,8 @@ class Oracle:
         for fn in ("oracle_decode", "oracle_decode_partials", "oracle_reduce", "oracle_prefill",
                    "oracle_mutant", "oracle_num_threads", "oracle_decode_f64kv",
                    "oracle_decode_partials_f64kv", "oracle_kv_append", "oracle_kv_append_fp8",
-                   "oracle_quantize_fp8", "oracle_fp8_dequant"):
+                   "oracle_quantize_fp8", "oracle_fp8_dequant", "oracle_kv_append_xpacked",
+                   "oracle_decode_xpacked", "oracle_decode_partials_xpacked"):
             getattr(lib, fn).restype = ctypes.c_int
         self.lib = lib
 
@@ -210,6 +218,60 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_decode_partials_f64kv rejected the shapes (status {rc})")
         return ml, es, to
+
+    # ---- O1 / O2 over the x-packed K / transposed V layouts -----------------
+    def decode_xpacked(self, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int,
+                       scale) -> np.ndarray:
+        """k_cache [num_blocks, H_kv, D/8, bs, 8], v_cache [num_blocks, H_kv, D, bs] (bf16 bits)."""
+        q = self._c(q, np.uint16)
+        S, Hq, D = q.shape
+        kc = self._c(k_cache, np.uint16)
+        bs = kc.shape[3]
+        bt = self._c(block_tables, np.int32)
+        out = np.empty((S, Hq, D), dtype=np.float64)
+        rc = self.lib.oracle_decode_xpacked(q, kc, self._c(v_cache, np.uint16), bt,
+                                            self._c(seq_lens, np.int32), S, Hq, num_kv_heads, D, bs,
+                                            bt.shape[1], float(np.float32(scale)), out)
+        if rc:
+            raise ValueError(f"oracle_decode_xpacked rejected the shapes (status {rc})")
+        return out
+
+    def decode_partials_xpacked(self, q, k_cache, v_cache, block_tables, seq_lens,
+                                num_kv_heads: int, scale, partition_size: int,
+                                max_num_partitions: Optional[int] = None):
+        q = self._c(q, np.uint16)
+        S, Hq, D = q.shape
+        kc = self._c(k_cache, np.uint16)
+        bs = kc.shape[3]
+        bt = self._c(block_tables, np.int32)
+        if max_num_partitions is None:
+            max_num_partitions = max(1, (bt.shape[1] * bs + partition_size - 1) // partition_size)
+        NP = int(max_num_partitions)
+        ml = np.full((S, Hq, NP), np.nan)
+        es = np.full((S, Hq, NP), np.nan)
+        to = np.full((S, Hq, NP, D), np.nan)
+        rc = self.lib.oracle_decode_partials_xpacked(q, kc, self._c(v_cache, np.uint16), bt,
+                                                     self._c(seq_lens, np.int32), S, Hq, num_kv_heads,
+                                                     D, bs, bt.shape[1], float(np.float32(scale)),
+                                                     int(partition_size), NP, ml, es, to)
+        if rc:
+            raise ValueError(f"oracle_decode_partials_xpacked rejected the shapes (status {rc})")
+        return ml, es, to
+
+    def kv_append_xpacked(self, k_new, v_new, block_tables, seq_lens, cu_seqlens, k_cache, v_cache):
+        """Copies of the x-packed K / transposed V caches with the new rows written."""
+        kn = self._c(k_new, np.uint16)
+        kc = np.array(k_cache, dtype=np.uint16, copy=True, order="C")
+        vc = np.array(v_cache, dtype=np.uint16, copy=True, order="C")
+        bt = self._c(block_tables, np.int32)
+        sl = self._c(seq_lens, np.int32)
+        _, Hkv, D, bs = vc.shape
+        rc = self.lib.oracle_kv_append_xpacked(kn, self._c(v_new, np.uint16), bt, sl,
+                                               self._c(cu_seqlens, np.int32), sl.shape[0], Hkv, D, bs,
+                                               bt.shape[1], kc, vc)
+        if rc:
+            raise ValueError(f"oracle_kv_append_xpacked rejected the inputs (status {rc})")
+        return kc, vc
 
     # ---- KV append ---------------------------------------------------------
     def kv_append(self, k_new, v_new, block_tables, seq_lens, cu_seqlens, k_cache, v_cache):

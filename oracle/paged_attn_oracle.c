@@ -63,14 +63,40 @@ static int kv_head_of(int h, int Hq, int Hkv) {
 #endif
 }
 
-/* A KV cache as the oracle reads it, [num_blocks, H_kv, block_size, D]:
- * bf16 bit patterns, or fp64 values (a dequantized FP8 cache). */
+/* A KV cache as the oracle reads it: bf16 bit patterns, or fp64 values (a
+ * dequantized FP8 cache).  Element (block, kv head, slot, d) lives at
+ *   layout 0: [num_blocks, H_kv, block_size, D]            (row-major tile)
+ *   layout 1: [num_blocks, H_kv, D / 8, block_size, 8]     (x-packed K)
+ *   layout 2: [num_blocks, H_kv, D, block_size]            (transposed V)
+ * (layouts 1 and 2 are the BI-V100 page's key and value caches, section 3
+ * "Paged K/V Gather", with x = 16 bytes / sizeof(bf16) = 8). */
+#define XPACK 8
 typedef struct {
     const uint16_t *bf16;
     const double *f64;
+    int layout, bs, D;
 } kv_cache_t;
 
-static double kv_elem(kv_cache_t c, long i) { return c.bf16 ? bf16_to_double(c.bf16[i]) : c.f64[i]; }
+/* Element offset of dim d of the row that starts at row-major offset `row`
+ * ((block * H_kv + head) * bs + slot) * D. */
+static long kv_index(kv_cache_t c, long row, int d) {
+    if (c.layout == 0) return row + d;
+    long tile = row / ((long)c.bs * c.D) * ((long)c.bs * c.D);
+    long slot = (row / c.D) % c.bs;
+    if (c.layout == 1) {
+#if ORACLE_MUTANT == 19
+        return tile + (long)(d % XPACK) * (c.bs * XPACK) + slot * XPACK + d / XPACK;
+#else
+        return tile + (long)(d / XPACK) * (c.bs * XPACK) + slot * XPACK + d % XPACK;
+#endif
+    }
+    return tile + (long)d * c.bs + slot;
+}
+
+static double kv_elem(kv_cache_t c, long row, int d) {
+    long i = kv_index(c, row, d);
+    return c.bf16 ? bf16_to_double(c.bf16[i]) : c.f64[i];
+}
 
 /* Element offset of token t's row of kv head g for sequence s: the logical
  * block t / bs is looked up in the block table, the slot is t % bs (RL.cu page,
@@ -101,7 +127,7 @@ static const uint16_t *q_row(const uint16_t *q, long row, int h, int Hq, int D, 
  * "Problem Definition": softmax(Q[h] K[t]^T / sqrt(d)) V[t]). */
 static double score(const uint16_t *qr, kv_cache_t k, long kr, int D, double scale) {
     double acc = 0.0;
-    for (int d = 0; d < D; ++d) acc += bf16_to_double(qr[d]) * kv_elem(k, kr + d);
+    for (int d = 0; d < D; ++d) acc += bf16_to_double(qr[d]) * kv_elem(k, kr, d);
 #if ORACLE_MUTANT == 1
     (void)scale;
     return acc;
@@ -143,9 +169,9 @@ static void attend_range(const uint16_t *qr, kv_cache_t k_cache, kv_cache_t v_ca
     for (int i = 0; i < n; ++i) {
         const long vr = kv_row(block_tables, s, t0 + i, g, Hkv, bs, D, mbps);
 #if ORACLE_MUTANT == 6
-        for (int d = 0; d < D; ++d) out[d] += z[i] * kv_elem(k_cache, vr + d);
+        for (int d = 0; d < D; ++d) out[d] += z[i] * kv_elem(k_cache, vr, d);
 #else
-        for (int d = 0; d < D; ++d) out[d] += z[i] * kv_elem(v_cache, vr + d);
+        for (int d = 0; d < D; ++d) out[d] += z[i] * kv_elem(v_cache, vr, d);
 #endif
     }
     for (int d = 0; d < D; ++d) out[d] /= l;
@@ -221,7 +247,7 @@ static int partials_impl(const uint16_t *q, kv_cache_t k_cache, kv_cache_t v_cac
 int oracle_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                   const int32_t *block_tables, const int32_t *seq_lens,
                   int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
-    kv_cache_t k = {k_cache, NULL}, v = {v_cache, NULL};
+    kv_cache_t k = {k_cache, NULL, 0, bs, D}, v = {v_cache, NULL, 0, bs, D};
     return decode_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, out);
 }
 
@@ -229,7 +255,7 @@ int oracle_decode_partials(const uint16_t *q, const uint16_t *k_cache, const uin
                            const int32_t *block_tables, const int32_t *seq_lens,
                            int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
                            int P, int NP, double *max_logits, double *exp_sums, double *tmp_out) {
-    kv_cache_t k = {k_cache, NULL}, v = {v_cache, NULL};
+    kv_cache_t k = {k_cache, NULL, 0, bs, D}, v = {v_cache, NULL, 0, bs, D};
     return partials_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, P, NP,
                          max_logits, exp_sums, tmp_out);
 }
@@ -239,7 +265,7 @@ int oracle_decode_partials(const uint16_t *q, const uint16_t *k_cache, const uin
 int oracle_decode_f64kv(const uint16_t *q, const double *k_cache, const double *v_cache,
                         const int32_t *block_tables, const int32_t *seq_lens,
                         int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
-    kv_cache_t k = {NULL, k_cache}, v = {NULL, v_cache};
+    kv_cache_t k = {NULL, k_cache, 0, bs, D}, v = {NULL, v_cache, 0, bs, D};
     return decode_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, out);
 }
 
@@ -248,7 +274,27 @@ int oracle_decode_partials_f64kv(const uint16_t *q, const double *k_cache, const
                                  int S, int Hq, int Hkv, int D, int bs, int mbps, float scale,
                                  int P, int NP, double *max_logits, double *exp_sums,
                                  double *tmp_out) {
-    kv_cache_t k = {NULL, k_cache}, v = {NULL, v_cache};
+    kv_cache_t k = {NULL, k_cache, 0, bs, D}, v = {NULL, v_cache, 0, bs, D};
+    return partials_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, P, NP,
+                         max_logits, exp_sums, tmp_out);
+}
+
+/* O1 and O2 over the BI-V100 page's cache layouts (x-packed K, transposed
+ * V; see kv_cache_t): the same definitions, only the element addresses
+ * differ. */
+int oracle_decode_xpacked(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                          const int32_t *block_tables, const int32_t *seq_lens,
+                          int S, int Hq, int Hkv, int D, int bs, int mbps, float scale, double *out) {
+    kv_cache_t k = {k_cache, NULL, 1, bs, D}, v = {v_cache, NULL, 2, bs, D};
+    return decode_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, out);
+}
+
+int oracle_decode_partials_xpacked(const uint16_t *q, const uint16_t *k_cache,
+                                   const uint16_t *v_cache, const int32_t *block_tables,
+                                   const int32_t *seq_lens, int S, int Hq, int Hkv, int D, int bs,
+                                   int mbps, float scale, int P, int NP, double *max_logits,
+                                   double *exp_sums, double *tmp_out) {
+    kv_cache_t k = {k_cache, NULL, 1, bs, D}, v = {v_cache, NULL, 2, bs, D};
     return partials_impl(q, k, v, block_tables, seq_lens, S, Hq, Hkv, D, bs, mbps, scale, P, NP,
                          max_logits, exp_sums, tmp_out);
 }
@@ -301,7 +347,7 @@ int oracle_prefill(const uint16_t *q, const uint16_t *k_bits, const uint16_t *v_
                    int S, int total_q, int Hq, int Hkv, int D, int bs, int mbps, float scale,
                    double *out) {
     if (Hq % Hkv != 0) return 2;
-    kv_cache_t k_cache = {k_bits, NULL}, v_cache = {v_bits, NULL};
+    kv_cache_t k_cache = {k_bits, NULL, 0, bs, D}, v_cache = {v_bits, NULL, 0, bs, D};
     long work = (long)total_q * Hq;
     for (long i = 0; i < work * D; ++i) out[i] = 0.0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -354,6 +400,40 @@ static long append_position(int c, int j) {
 #else
     return (long)c + j;
 #endif
+}
+
+static int kv_append_impl(const uint16_t *k_new, const uint16_t *v_new,
+                          const int32_t *block_tables, const int32_t *seq_lens,
+                          const int32_t *cu_seqlens, int S, int Hkv, int D, int bs, int mbps,
+                          uint16_t *k_cache, uint16_t *v_cache, int k_layout, int v_layout) {
+    kv_cache_t kl = {NULL, NULL, k_layout, bs, D}, vl = {NULL, NULL, v_layout, bs, D};
+    for (int s = 0; s < S; ++s) {
+        int n = cu_seqlens[s + 1] - cu_seqlens[s];
+        int c = seq_lens[s] - n;
+        if (c < 0) return 2;
+        for (int j = 0; j < n; ++j) {
+            long pos = append_position(c, j);
+            if (pos / bs >= mbps) continue;
+            for (int g = 0; g < Hkv; ++g) {
+                long dst = kv_row(block_tables, s, (int)pos, g, Hkv, bs, D, mbps);
+                long src = ((long)(cu_seqlens[s] + j) * Hkv + g) * D;
+                for (int d = 0; d < D; ++d) {
+                    k_cache[kv_index(kl, dst, d)] = k_new[src + d];
+                    v_cache[kv_index(vl, dst, d)] = v_new[src + d];
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* KV append into the BI-V100 page's layouts (x-packed K, transposed V). */
+int oracle_kv_append_xpacked(const uint16_t *k_new, const uint16_t *v_new,
+                             const int32_t *block_tables, const int32_t *seq_lens,
+                             const int32_t *cu_seqlens, int S, int Hkv, int D, int bs, int mbps,
+                             uint16_t *k_cache, uint16_t *v_cache) {
+    return kv_append_impl(k_new, v_new, block_tables, seq_lens, cu_seqlens, S, Hkv, D, bs, mbps,
+                          k_cache, v_cache, 1, 2);
 }
 
 int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *block_tables,

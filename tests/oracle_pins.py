@@ -548,6 +548,60 @@ def pin_fp8_kv_append_refills_erased_rows(orc):
     assert np.array_equal(ks2, eks, equal_nan=True) and np.array_equal(vs2, evs, equal_nan=True)
 
 
+# --------------------------------------------------------------------------
+# the BI-V100 page's cache layouts: x-packed K, transposed V
+# --------------------------------------------------------------------------
+def to_xpacked(kcache, vcache, x=8):
+    """Row-major [blocks, H, bs, D] caches -> K [blocks, H, D/x, bs, x] and
+    V [blocks, H, D, bs], by reshaping and transposing (the test's own layout
+    conversion, independent of the oracle's address arithmetic)."""
+    nb, H, bs, D = kcache.shape
+    k = np.ascontiguousarray(kcache.reshape(nb, H, bs, D // x, x).transpose(0, 1, 3, 2, 4))
+    v = np.ascontiguousarray(vcache.transpose(0, 1, 3, 2))
+    return k, v
+
+
+def pin_xpacked_decode_brute_force(orc):
+    for seed, Hq, Hkv, D, lens in [(71, 4, 2, 16, [1, 16, 17, 40]), (72, 6, 2, 32, [70, 9])]:
+        q, kc, vc, kcache, vcache, bt, sl = _tiny_decode_problem(seed, Hq, Hkv, D, lens)
+        kx, vx = to_xpacked(kcache, vcache)
+        scale = np.float32(1.0 / math.sqrt(D))
+        out = orc.decode_xpacked(q, kx, vx, bt, sl, Hkv, scale)
+        G = Hq // Hkv
+        for s, L in enumerate(lens):
+            K, V = _f(kc[s]), _f(vc[s])
+            for h in range(Hq):
+                ref, _, _ = brute_attention(_f(q[s, h]), K, V, h // G, float(scale), L)
+                _close(out[s, h], ref, 1e-12, f"x-packed decode seed {seed} s{s} h{h}")
+
+
+def pin_xpacked_equals_row_major(orc):
+    """The same cache in both layouts gives bit-identical outputs and partials."""
+    case = workloads.build_case("xpack", 73, [1, 33, 130, 512], 8, 2, 64)
+    kx, vx = to_xpacked(case.k_cache, case.v_cache)
+    a = orc.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, 2, case.scale)
+    b = orc.decode_xpacked(case.q, kx, vx, case.block_tables, case.seq_lens, 2, case.scale)
+    assert np.array_equal(a, b)
+    pa_ = orc.decode_partials(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, 2,
+                              case.scale, 64)
+    pb_ = orc.decode_partials_xpacked(case.q, kx, vx, case.block_tables, case.seq_lens, 2, case.scale, 64)
+    for u, w in zip(pa_, pb_):
+        assert np.array_equal(np.nan_to_num(u), np.nan_to_num(w))
+
+
+def pin_xpacked_append_refills_erased_rows(orc):
+    lens, n_new, bs = [37, 16, 1, 70], [5, 16, 1, 0], 16
+    kc, vc, kcache, vcache, bt, sl, cu, k_new, v_new = _append_problem(74, 2, 16, lens, n_new)
+    kx, vx = to_xpacked(kcache, vcache)
+    k_er, v_er = kcache.copy(), vcache.copy()
+    for b, t in _slots_of_new_rows(bt, lens, n_new, bs):
+        k_er[b, :, t] = 0x7FC0
+        v_er[b, :, t] = 0x7FC0
+    kex, vex = to_xpacked(k_er, v_er)
+    k2, v2 = orc.kv_append_xpacked(k_new, v_new, bt, sl, cu, kex, vex)
+    assert np.array_equal(k2, kx) and np.array_equal(v2, vx), "x-packed append did not restore the cache"
+
+
 PINS: Dict[str, Callable] = {name: fn for name, fn in sorted(globals().items())
                              if name.startswith("pin_") and callable(fn)}
 

@@ -6,7 +6,7 @@ K used as V, a dropped denominator term, unnormalized partials, overlapping
 partitions, a merge without exp_sum weights, a dropped causal diagonal,
 top-left causal alignment, a shifted query row, a transposed query index,
 FP8 ties away from zero, a wrong FP8 scale, a late append position, FP8
-subnormals dropped).
+subnormals dropped, a swapped x-packed K index).
 Every build runs the pin suite in a child process (a mutant may crash); the
 test requires at least one failing pin or a crash for each.
 """
@@ -38,6 +38,7 @@ MUTANTS = {
     16: "FP8 scale from the wrong largest magnitude (240)",
     17: "append one position late",
     18: "FP8 subnormals read as zero",
+    19: "x-packed K index with chunk and lane swapped",
 }
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
