@@ -1,7 +1,8 @@
 /*
  * paged_attn.h -- C ABI of the MI355X (gfx950) paged GQA attention library.
  *
- * Three device entry points plus host helpers.  All pointers to tensors are
+ * Device entry points (decode, merge, prefill, cache writes; bf16, FP8 and
+ * x-packed cache variants) plus host helpers.  All pointers to tensors are
  * DEVICE pointers owned by the caller; the library never allocates, frees or
  * synchronizes.  Work is enqueued on `stream` (a hipStream_t passed as void*;
  * NULL = the default stream).  Every entry point validates its scalar
@@ -143,6 +144,22 @@ int paged_attn_decode_fp8(const void *q, const void *k_cache, const void *v_cach
                           int max_num_partitions, void *stream);
 
 /*
+ * Paged GQA decode over the BI-V100 page's cache layouts (section 3 "Paged
+ * K/V Gather"): x-packed K and transposed V, bf16, x = 16 bytes / 2 = 8:
+ *   k_cache  bf16 [num_blocks, H_kv, D / 8, block_size, 8]
+ *   v_cache  bf16 [num_blocks, H_kv, D, block_size]
+ * Element (block, h, slot, d) of K is k_cache[block, h, d / 8, slot, d % 8]
+ * and of V is v_cache[block, h, d, slot].  Same computation, other arguments,
+ * partials, merge and status codes as paged_attn_decode.
+ */
+int paged_attn_decode_xpacked(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, float scale,
+                              int partition_size, void *out, float *max_logits, float *exp_sums,
+                              float *tmp_out, int max_num_partitions, void *stream);
+
+/*
  * KV append: writes the K/V rows of new tokens into their cache slots -- the
  * cache write before decode and prefill (the AstrAI page's backend layer "owns
  * KV cache writes and reads").  Sequence s owns rows [cu_seqlens[s],
@@ -164,6 +181,17 @@ int paged_attn_kv_append(const void *k_new, const void *v_new, const int32_t *bl
                          int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
                          int block_size, int num_blocks, int max_blocks_per_seq, void *k_cache,
                          void *v_cache, void *stream);
+
+/*
+ * KV append into the x-packed K / transposed V layouts of
+ * paged_attn_decode_xpacked: the same rows, placement, arguments and status
+ * codes as paged_attn_kv_append.
+ */
+int paged_attn_kv_append_xpacked(const void *k_new, const void *v_new, const int32_t *block_tables,
+                                 const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs,
+                                 int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
+                                 int block_size, int num_blocks, int max_blocks_per_seq,
+                                 void *k_cache, void *v_cache, void *stream);
 
 /*
  * KV append into an FP8 cache (the B200 page, "FP8 KV Quantize/Dequant", with

@@ -58,6 +58,8 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_decode_fp8.argtypes = [_vp] * 7 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp]
         lib.paged_attn_kv_append.argtypes = [_vp] * 5 + [_i] * 8 + [_vp] * 3
         lib.paged_attn_kv_append_fp8.argtypes = [_vp] * 5 + [_i] * 8 + [_vp] * 5
+        lib.paged_attn_decode_xpacked.argtypes = lib.paged_attn_decode.argtypes
+        lib.paged_attn_kv_append_xpacked.argtypes = lib.paged_attn_kv_append.argtypes
         lib.paged_attn_prefill_ragged.argtypes = [_vp] * 6 + [_i] * 9 + [ctypes.c_float, _vp, _vp]
         lib.paged_attn_prefill_ragged_split.argtypes = ([_vp] * 6 + [_i] * 9 + [ctypes.c_float, _i, _vp,
                                                           ctypes.c_longlong, _vp, _vp])
@@ -71,6 +73,7 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_status_string.restype = ctypes.c_char_p
         for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
                    "paged_attn_decode_fp8", "paged_attn_kv_append", "paged_attn_kv_append_fp8",
+                   "paged_attn_decode_xpacked", "paged_attn_kv_append_xpacked",
                    "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
                    "paged_attn_prefill_chunk_size",
                    "paged_attn_num_partitions", "paged_attn_choose_partition_size",
@@ -211,6 +214,53 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, k_scales, v_scales, block_tables,
         int(partition_size), _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
         int(max_num_partitions), _stream(stream))
     _check("paged_attn_decode_fp8", st)
+
+
+def paged_attn_decode_xpacked(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                              partition_size: int = 0, out=None, max_logits=None, exp_sums=None,
+                              tmp_out=None, max_num_partitions: Optional[int] = None,
+                              stream=None) -> None:
+    """Decode over the x-packed K [num_blocks, H_kv, D/8, bs, 8] and transposed
+    V [num_blocks, H_kv, D, bs] caches (bf16)."""
+    import torch
+    _want(q, torch.bfloat16, "q")
+    _want(k_cache, torch.bfloat16, "k_cache")
+    _want(v_cache, torch.bfloat16, "v_cache")
+    _want(block_tables, torch.int32, "block_tables")
+    _want(seq_lens, torch.int32, "seq_lens")
+    _want(out, torch.bfloat16, "out")
+    for name, t in (("max_logits", max_logits), ("exp_sums", exp_sums), ("tmp_out", tmp_out)):
+        _want(t, torch.float32, name)
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, H_kv, D/8, bs, 8] and v_cache [num_blocks, H_kv, D, bs]")
+    num_seqs, hq, d = q.shape
+    num_blocks, hkv, _, bs = v_cache.shape
+    if max_num_partitions is None:
+        max_num_partitions = tmp_out.shape[2] if tmp_out is not None else 1
+    st = library().paged_attn_decode_xpacked(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), num_seqs, hq,
+        hkv, d, bs, num_blocks, block_tables.shape[1], float(scale), int(partition_size),
+        _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), int(max_num_partitions),
+        _stream(stream))
+    _check("paged_attn_decode_xpacked", st)
+
+
+def paged_attn_kv_append_xpacked(k_new, v_new, block_tables, seq_lens, cu_seqlens,
+                                 max_new_tokens: int, k_cache, v_cache, stream=None) -> None:
+    """Write new rows (bf16 [num_tokens, H_kv, D]) into x-packed K / transposed V caches."""
+    import torch
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _want(t, torch.bfloat16, name)
+    _want(block_tables, torch.int32, "block_tables")
+    _want(seq_lens, torch.int32, "seq_lens")
+    _want(cu_seqlens, torch.int32, "cu_seqlens")
+    num_tokens, hkv, d = k_new.shape
+    num_blocks, _, _, bs = v_cache.shape
+    st = library().paged_attn_kv_append_xpacked(
+        _ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(seq_lens), _ptr(cu_seqlens),
+        seq_lens.shape[0], num_tokens, int(max_new_tokens), hkv, d, bs, num_blocks,
+        block_tables.shape[1], _ptr(k_cache), _ptr(v_cache), _stream(stream))
+    _check("paged_attn_kv_append_xpacked", st)
 
 
 def paged_attn_kv_append(k_new, v_new, block_tables, seq_lens, cu_seqlens, max_new_tokens: int,

@@ -137,7 +137,7 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
                   int max_blocks_per_seq, float scale, int partition_size, void *out,
                   float *max_logits, float *exp_sums, float *tmp_out, int max_num_partitions,
                   int32_t *counters, void *stream, const float *k_scales = nullptr,
-                  const float *v_scales = nullptr) {
+                  const float *v_scales = nullptr, bool xpacked = false) {
     int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
     if (st != PA_OK) return st;
@@ -181,7 +181,7 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
     a.k_scales = k_scales;
     a.v_scales = v_scales;
     a.stream = static_cast<hipStream_t>(stream);
-    const hipError_t e = fp8 ? pa::launch_decode_fp8(a) : pa::launch_decode(a);
+    const hipError_t e = fp8 ? pa::launch_decode_fp8(a) : xpacked ? pa::launch_decode_xpacked(a) : pa::launch_decode(a);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -189,7 +189,7 @@ int append_common(const void *k_new, const void *v_new, const int32_t *block_tab
                   const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs, int num_tokens,
                   int max_new_tokens, int num_kv_heads, int head_dim, int block_size,
                   int num_blocks, int max_blocks_per_seq, void *k_cache, void *v_cache,
-                  float *k_scales, float *v_scales, bool fp8, void *stream) {
+                  float *k_scales, float *v_scales, bool fp8, void *stream, bool xpacked = false) {
     if (!k_new || !v_new || !block_tables || !seq_lens || !cu_seqlens || !k_cache || !v_cache)
         return PA_ERR_NULL_POINTER;
     if (fp8 && (!k_scales || !v_scales)) return PA_ERR_NULL_POINTER;
@@ -219,7 +219,8 @@ int append_common(const void *k_new, const void *v_new, const int32_t *block_tab
     a.k_scales = k_scales;
     a.v_scales = v_scales;
     a.stream = static_cast<hipStream_t>(stream);
-    const hipError_t e = fp8 ? pa::launch_kv_append_fp8(a) : pa::launch_kv_append(a);
+    const hipError_t e = fp8 ? pa::launch_kv_append_fp8(a)
+                             : xpacked ? pa::launch_kv_append_xpacked(a) : pa::launch_kv_append(a);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 }  // namespace
@@ -446,6 +447,29 @@ int paged_attn_prefill_ragged_split(const void *q, const void *k_cache, const vo
     }
     a.stream = static_cast<hipStream_t>(stream);
     return pa::launch_prefill(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+
+int paged_attn_decode_xpacked(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, float scale,
+                              int partition_size, void *out, float *max_logits, float *exp_sums,
+                              float *tmp_out, int max_num_partitions, void *stream) {
+    return decode_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                         partition_size, out, max_logits, exp_sums, tmp_out, max_num_partitions,
+                         nullptr, stream, nullptr, nullptr, true);
+}
+
+int paged_attn_kv_append_xpacked(const void *k_new, const void *v_new, const int32_t *block_tables,
+                                 const int32_t *seq_lens, const int32_t *cu_seqlens, int num_seqs,
+                                 int num_tokens, int max_new_tokens, int num_kv_heads, int head_dim,
+                                 int block_size, int num_blocks, int max_blocks_per_seq,
+                                 void *k_cache, void *v_cache, void *stream) {
+    return append_common(k_new, v_new, block_tables, seq_lens, cu_seqlens, num_seqs, num_tokens,
+                         max_new_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_blocks_per_seq, k_cache, v_cache, nullptr, nullptr, false, stream, true);
 }
 
 }  // extern "C"

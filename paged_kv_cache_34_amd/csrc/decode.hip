@@ -11,7 +11,7 @@ namespace {
 constexpr int kReduceWaves = 4;
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a) { return launch_detail::launch_decode_t<false>(a); }
+hipError_t launch_decode(const DecodeArgs &a) { return launch_detail::launch_decode_t<false, false>(a); }
 
 hipError_t launch_reduce(const ReduceArgs &a) {
     const int rows = 256 / a.head_dim;  // rows of the one-wave merge

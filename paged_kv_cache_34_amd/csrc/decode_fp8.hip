@@ -4,6 +4,6 @@
 
 namespace pa {
 
-hipError_t launch_decode_fp8(const DecodeArgs &a) { return launch_detail::launch_decode_t<true>(a); }
+hipError_t launch_decode_fp8(const DecodeArgs &a) { return launch_detail::launch_decode_t<true, false>(a); }
 
 }  // namespace pa

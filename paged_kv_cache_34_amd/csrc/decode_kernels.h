@@ -195,13 +195,14 @@ __device__ __forceinline__ void lds_barrier() {
 //                  product keeps ~16 mantissa bits) -> lane holds dims
 //                  16 dt + 4 grp + i of head col.
 // Lanes with col >= G carry a copy of head 0; their results are never stored.
-template <int D, int G, int NW, int DEPTH, bool ONE_CHUNK, bool FP8>
+template <int D, int G, int NW, int DEPTH, bool ONE_CHUNK, bool FP8, bool XP>
 __device__ __forceinline__ void decode_item(const DecodeParams &prm, const DecodeItem &it,
                                             const DecodeItem &nx, bool has_next, bool primed,
                                             u32x4 (&qb)[D / 32],
                                             u32x4 (&kbuf)[DEPTH + 1][KvWords<D, FP8>::N],
                                             u32x4 (&vbuf)[DEPTH + 1][KvWords<D, FP8>::N], float *lds) {
     using S = DecodeShape<D, G, NW>;
+    static_assert(!(FP8 && XP), "the x-packed layout holds bf16");
     constexpr int NJ = S::NJ, NDT = S::NDT, VROW = S::VROW;
     constexpr int NW16 = KvWords<D, FP8>::N;      // words per ring slot
     // V tile loads: a token row is LPT lanes of 16 bytes (8 bf16 or 16 E4M3
@@ -245,8 +246,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     const char *kv_k = kc + kvh * tile, *kv_v = vc + kvh * tile;
     const char *nx_k = kc + nx_kvh * tile, *nx_v = vc + nx_kvh * tile;
     // bytes within a tile: K lane = (token col, chunk grp (+ 4j)); V lane = (row vrow, chunk vcol)
-    const int k_voff = FP8 ? col * D + 16 * grp : (col * D + grp * 8) * 2;
-    const int v_voff = (vrow * D * EB) + vcol * 16;
+    // (x-packed K [D/8][16][8]: chunk 4j + grp of token col at ((4j + grp) * 16 + col) * 16 bytes;
+    //  transposed V [D][16]: the PV A operand of dims 16 dt + col, tokens 4 grp + 0..3 is the
+    //  8 bytes at (16 dt + col) * 32 + 8 grp)
+    const int k_voff = FP8 ? col * D + 16 * grp : XP ? (grp * 16 + col) * 16 : (col * D + grp * 8) * 2;
+    const int v_voff = XP ? col * 32 + 8 * grp : (vrow * D * EB) + vcol * 16;
     // FP8 scales: [num_blocks, H_kv, 16] floats, the lane's 4 score tokens 4 grp + 0..3
     const float *ks_cur = FP8 ? prm.k_scales + kvh * kBlock : nullptr;
     const float *vs_cur = FP8 ? prm.v_scales + kvh * kBlock : nullptr;
@@ -287,10 +291,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
                                                            0, bytes, kBufferFlags);
 #pragma unroll
         for (int j2 = 0; j2 < NK; ++j2)
-            kr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + j2 * 64, 0, 0));
+            kr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + j2 * (XP ? 1024 : 64), 0, 0));
+        if constexpr (XP) {
 #pragma unroll
-        for (int j2 = 0; j2 < NV; ++j2)
-            vr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + j2 * TPI * D * EB, 0, 0));
+            for (int dt = 0; dt < NDT; ++dt) {
+                const auto w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, v_voff + dt * 512, 0, 0));
+                vr[dt >> 1][2 * (dt & 1)] = w[0];
+                vr[dt >> 1][2 * (dt & 1) + 1] = w[1];
+            }
+        } else {
+#pragma unroll
+            for (int j2 = 0; j2 < NV; ++j2)
+                vr[j2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + j2 * TPI * D * EB, 0, 0));
+        }
         if constexpr (FP8) {
             const int sbytes = (cur || nxt) ? kBlock * 4 : 0;
             const auto ksr = __builtin_amdgcn_make_buffer_rsrc((void *)((cur ? ks_cur : ks_nx) + phys * sc_stride),
@@ -306,9 +319,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         const int tb = (b_begin + wave + NW * i) * kBlock;  // logical index of slot 0
         const bool tail = tb + kBlock > t_end;
         // stage V as bf16 (FP8 codes converted exactly; token rows past the end
-        // are zeroed so stale slots never reach PV)
+        // are zeroed so stale slots never reach PV); the x-packed layout's V
+        // is already the PV operand
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
+        for (int j = 0; j < (XP ? 0 : NV); ++j) {
             const bool dead = tail && tb + vrow + j * TPI >= t_end;
             if constexpr (FP8) {
                 const u32x4 w = vr[j];
@@ -366,15 +380,32 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         const uint32_t l23 = cvt_pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
         const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
         const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
-        wave_lds_sync();
+        if constexpr (XP) {
+            // the lane's 4 tokens of each V operand: zero those past the end
+            uint32_t keep0 = 0xffffffffu, keep1 = 0xffffffffu;
+            if (tail) {
+                const int t0 = tb + 4 * grp;
+                keep0 = (t0 < t_end ? 0x0000ffffu : 0u) | (t0 + 1 < t_end ? 0xffff0000u : 0u);
+                keep1 = (t0 + 2 < t_end ? 0x0000ffffu : 0u) | (t0 + 3 < t_end ? 0xffff0000u : 0u);
+            }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)(vst_rd + dt * 16));
-            oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, oT[dt], 0, 0, 0);
-            oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, oT[dt], 0, 0, 0);
+            for (int dt = 0; dt < NDT; ++dt) {
+                const u32x2 w = {vr[dt >> 1][2 * (dt & 1)] & keep0, vr[dt >> 1][2 * (dt & 1) + 1] & keep1};
+                const s16x4 a = __builtin_bit_cast(s16x4, w);
+                oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, oT[dt], 0, 0, 0);
+                oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, oT[dt], 0, 0, 0);
+            }
+        } else {
+            wave_lds_sync();
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)(vst_rd + dt * 16));
+                oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, oT[dt], 0, 0, 0);
+                oT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, oT[dt], 0, 0, 0);
+            }
+            wave_lds_sync();
         }
-        wave_lds_sync();
     };
 
     if (!primed) {
@@ -588,7 +619,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
 
 // One workgroup per (partition, kv head, sequence); workgroups whose partition
 // starts past the sequence end exit at once.
-template <int D, int G, int NW, int DEPTH, bool FP8>
+template <int D, int G, int NW, int DEPTH, bool FP8, bool XP>
 __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams prm) {
     using S = DecodeShape<D, G, NW>;
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
@@ -605,7 +636,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const DecodeItem it = make_item<NW>(prm, seq, kvh, part, L, wave, threadIdx.x & 63);
     u32x4 qb[D / 32], kbuf[DEPTH + 1][KvWords<D, FP8>::N], vbuf[DEPTH + 1][KvWords<D, FP8>::N];
-    decode_item<D, G, NW, DEPTH, false, FP8>(prm, it, it, false, false, qb, kbuf, vbuf, lds);
+    decode_item<D, G, NW, DEPTH, false, FP8, XP>(prm, it, it, false, false, qb, kbuf, vbuf, lds);
 }
 
 // Compact persistent split-KV: every workgroup first builds, in LDS, the
@@ -616,7 +647,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
 // issues the next one's query rows and first K/V tiles before its epilogue.
 constexpr int kCompactMaxSeqs = 1024;
 
-template <int D, int G, int NW, int DEPTH, bool FP8>
+template <int D, int G, int NW, int DEPTH, bool FP8, bool XP>
 __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodeParams prm) {
     using S = DecodeShape<D, G, NW>;
     constexpr int T = NW * 64;
@@ -692,7 +723,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
         const int next = item + gridDim.x;
         const bool has_next = next < total;
         const DecodeItem nx = has_next ? locate(next) : it;
-        decode_item<D, G, NW, DEPTH, true, FP8>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
+        decode_item<D, G, NW, DEPTH, true, FP8, XP>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
         if (!has_next) break;
         item = next;
         it = nx;
@@ -947,7 +978,7 @@ inline int cu_count() {
     return cached[dev];
 }
 
-template <int D, int G, bool FP8>
+template <int D, int G, bool FP8, bool XP>
 hipError_t launch_decode_dg(const DecodeArgs &a) {
     constexpr int DEPTH = decode_depth(D, FP8);
     DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
@@ -960,54 +991,55 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
         if (per_cu == 0) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8>, block.x, 0) != hipSuccess || n <= 0)
+                    &n, paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP>, block.x, 0) != hipSuccess || n <= 0)
                 n = 1;
             per_cu = PA_DECODE_PERSIST_PER_CU > 0 ? PA_DECODE_PERSIST_PER_CU : n;
         }
         const long upper = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
         const long cap = (long)cu_count() * per_cu;
         dim3 grid((unsigned)(upper < cap ? upper : cap));
-        hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8>), grid, block, 0,
+        hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP>), grid, block, 0,
                            a.stream, prm);
     } else {
         dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-        hipLaunchKernelGGL((paged_decode_grid_kernel<D, G, kDecodeWaves, DEPTH, FP8>), grid, block, 0,
+        hipLaunchKernelGGL((paged_decode_grid_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP>), grid, block, 0,
                            a.stream, prm);
     }
     return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool XP>
 hipError_t launch_decode_d(const DecodeArgs &a, int G) {
     switch (G) {
-        case 1: return launch_decode_dg<D, 1, FP8>(a);
-        case 2: return launch_decode_dg<D, 2, FP8>(a);
-        case 3: return launch_decode_dg<D, 3, FP8>(a);
-        case 4: return launch_decode_dg<D, 4, FP8>(a);
-        case 5: return launch_decode_dg<D, 5, FP8>(a);
-        case 6: return launch_decode_dg<D, 6, FP8>(a);
-        case 7: return launch_decode_dg<D, 7, FP8>(a);
-        case 8: return launch_decode_dg<D, 8, FP8>(a);
-        case 9: return launch_decode_dg<D, 9, FP8>(a);
-        case 10: return launch_decode_dg<D, 10, FP8>(a);
-        case 11: return launch_decode_dg<D, 11, FP8>(a);
-        case 12: return launch_decode_dg<D, 12, FP8>(a);
-        case 13: return launch_decode_dg<D, 13, FP8>(a);
-        case 14: return launch_decode_dg<D, 14, FP8>(a);
-        case 15: return launch_decode_dg<D, 15, FP8>(a);
-        case 16: return launch_decode_dg<D, 16, FP8>(a);
+        case 1: return launch_decode_dg<D, 1, FP8, XP>(a);
+        case 2: return launch_decode_dg<D, 2, FP8, XP>(a);
+        case 3: return launch_decode_dg<D, 3, FP8, XP>(a);
+        case 4: return launch_decode_dg<D, 4, FP8, XP>(a);
+        case 5: return launch_decode_dg<D, 5, FP8, XP>(a);
+        case 6: return launch_decode_dg<D, 6, FP8, XP>(a);
+        case 7: return launch_decode_dg<D, 7, FP8, XP>(a);
+        case 8: return launch_decode_dg<D, 8, FP8, XP>(a);
+        case 9: return launch_decode_dg<D, 9, FP8, XP>(a);
+        case 10: return launch_decode_dg<D, 10, FP8, XP>(a);
+        case 11: return launch_decode_dg<D, 11, FP8, XP>(a);
+        case 12: return launch_decode_dg<D, 12, FP8, XP>(a);
+        case 13: return launch_decode_dg<D, 13, FP8, XP>(a);
+        case 14: return launch_decode_dg<D, 14, FP8, XP>(a);
+        case 15: return launch_decode_dg<D, 15, FP8, XP>(a);
+        case 16: return launch_decode_dg<D, 16, FP8, XP>(a);
         default: return hipErrorInvalidValue;
     }
 }
 
-// Decode launch for a bf16 (FP8 false) or FP8 cache.
-template <bool FP8>
+// Decode launch for a bf16 (FP8 false) or FP8 cache, in the row-major tile
+// layout or (XP) the x-packed K / transposed V layout.
+template <bool FP8, bool XP>
 hipError_t launch_decode_t(const DecodeArgs &a) {
     const int G = a.num_q_heads / a.num_kv_heads;
     switch (a.head_dim) {
-        case 64: return launch_decode_d<64, FP8>(a, G);
-        case 128: return launch_decode_d<128, FP8>(a, G);
-        case 256: return launch_decode_d<256, FP8>(a, G);
+        case 64: return launch_decode_d<64, FP8, XP>(a, G);
+        case 128: return launch_decode_d<128, FP8, XP>(a, G);
+        case 256: return launch_decode_d<256, FP8, XP>(a, G);
         default: return hipErrorInvalidValue;
     }
 }

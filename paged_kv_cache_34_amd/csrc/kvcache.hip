@@ -10,7 +10,8 @@
 // c + j (c = seq_lens[s] - n), block table entry (c + j) / 16, slot
 // (c + j) % 16 -- where the prefill kernel expects the rows it attends to.
 //
-// Both kernels are HBM-bound copies: grid (token groups, sequences), each
+// The bf16 kernel also writes the BI-V100 page's layouts (x-packed K,
+// transposed V).  Both kernels are HBM-bound copies: grid (token groups, sequences), each
 // workgroup moving kAppendTokens new tokens with 16-byte loads and stores.
 #include "pa_common.h"
 #include "pa_launch.h"
@@ -23,8 +24,11 @@ constexpr int kAppendThreads = 256;
 constexpr int kSlots = 16;           // tokens per cache block
 constexpr float kE4m3Max = 448.0f;   // largest finite E4M3 magnitude
 
-// bf16: every (token, K/V, kv head, 16-byte chunk) is one copy.
-template <int D>
+// bf16: every (token, K/V, kv head, 16-byte chunk) is one copy.  In the
+// BI-V100 page's layouts (XP) the K chunk lands at its x-packed place
+// [D/8][16][8] (still 16 contiguous bytes) and the V chunk's 8 values are
+// scattered down the token column of the transposed tile [D][16].
+template <int D, bool XP>
 __global__ __launch_bounds__(kAppendThreads) void paged_kv_append_kernel(AppendArgs a) {
     const int s = blockIdx.y;
     const int row0 = a.cu_seqlens[s];
@@ -50,9 +54,21 @@ __global__ __launch_bounds__(kAppendThreads) void paged_kv_append_kernel(AppendA
         const int j = j0 + tj, pos = c + j;
         const long phys = bt[pos / kSlots];
         const long src = ((long)(row0 + j) * hkv + h) * D + ch * 8;
-        const long dst = ((phys * hkv + h) * kSlots + pos % kSlots) * D + ch * 8;
-        *reinterpret_cast<u32x4 *>((is_v ? vc : kc) + dst) =
-            *reinterpret_cast<const u32x4 *>((is_v ? vn : kn) + src);
+        const u32x4 w = *reinterpret_cast<const u32x4 *>((is_v ? vn : kn) + src);
+        if constexpr (XP) {
+            const long tile = (phys * hkv + h) * kSlots * D;
+            const int slot = pos % kSlots;
+            if (!is_v) {
+                *reinterpret_cast<u32x4 *>(kc + tile + (ch * kSlots + slot) * 8) = w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    vc[tile + (ch * 8 + e) * kSlots + slot] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            }
+        } else {
+            const long dst = ((phys * hkv + h) * kSlots + pos % kSlots) * D + ch * 8;
+            *reinterpret_cast<u32x4 *>((is_v ? vc : kc) + dst) = w;
+        }
     }
 }
 
@@ -148,22 +164,23 @@ __global__ __launch_bounds__(kAppendThreads) void paged_kv_append_fp8_kernel(App
     }
 }
 
-template <bool FP8>
+template <bool FP8, bool XP>
 hipError_t launch_append(const AppendArgs &a) {
+    static_assert(!(FP8 && XP), "the x-packed layout holds bf16");
     dim3 grid((a.max_new_tokens + kAppendTokens - 1) / kAppendTokens, a.num_seqs);
     dim3 block(kAppendThreads);
     switch (a.head_dim) {
         case 64:
-            hipLaunchKernelGGL(FP8 ? paged_kv_append_fp8_kernel<64> : paged_kv_append_kernel<64>, grid, block, 0,
-                               a.stream, a);
+            hipLaunchKernelGGL((FP8 ? paged_kv_append_fp8_kernel<64> : paged_kv_append_kernel<64, XP>), grid, block,
+                               0, a.stream, a);
             break;
         case 128:
-            hipLaunchKernelGGL(FP8 ? paged_kv_append_fp8_kernel<128> : paged_kv_append_kernel<128>, grid, block,
-                               0, a.stream, a);
+            hipLaunchKernelGGL((FP8 ? paged_kv_append_fp8_kernel<128> : paged_kv_append_kernel<128, XP>), grid,
+                               block, 0, a.stream, a);
             break;
         case 256:
-            hipLaunchKernelGGL(FP8 ? paged_kv_append_fp8_kernel<256> : paged_kv_append_kernel<256>, grid, block,
-                               0, a.stream, a);
+            hipLaunchKernelGGL((FP8 ? paged_kv_append_fp8_kernel<256> : paged_kv_append_kernel<256, XP>), grid,
+                               block, 0, a.stream, a);
             break;
         default: return hipErrorInvalidValue;
     }
@@ -172,7 +189,8 @@ hipError_t launch_append(const AppendArgs &a) {
 
 }  // namespace
 
-hipError_t launch_kv_append(const AppendArgs &a) { return launch_append<false>(a); }
-hipError_t launch_kv_append_fp8(const AppendArgs &a) { return launch_append<true>(a); }
+hipError_t launch_kv_append(const AppendArgs &a) { return launch_append<false, false>(a); }
+hipError_t launch_kv_append_fp8(const AppendArgs &a) { return launch_append<true, false>(a); }
+hipError_t launch_kv_append_xpacked(const AppendArgs &a) { return launch_append<false, true>(a); }
 
 }  // namespace pa

@@ -74,9 +74,11 @@ struct AppendArgs {
 
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_decode_fp8(const DecodeArgs &a);
+hipError_t launch_decode_xpacked(const DecodeArgs &a);
 hipError_t launch_reduce(const ReduceArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
 hipError_t launch_kv_append(const AppendArgs &a);
 hipError_t launch_kv_append_fp8(const AppendArgs &a);
+hipError_t launch_kv_append_xpacked(const AppendArgs &a);
 
 }  // namespace pa

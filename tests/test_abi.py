@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_prefill_chunk_size", "paged_attn_prefill_workspace_size",
         "paged_attn_num_partitions", "paged_attn_choose_partition_size",
         "paged_attn_prefill_tile_map", "paged_attn_status_string", "paged_attn_decode_fp8",
-        "paged_attn_kv_append", "paged_attn_kv_append_fp8"} | (
+        "paged_attn_kv_append", "paged_attn_kv_append_fp8", "paged_attn_decode_xpacked",
+        "paged_attn_kv_append_xpacked"} | (
         set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
     for name in names:
         assert hasattr(lib, name), name
@@ -312,3 +313,39 @@ def test_kv_append_fp8_needs_scales(lib):
     assert append_call(lib, True, vs=FAKE + 4) == pa.PA_ERR_ALIGNMENT
     # the bf16 form takes no scales: its validation never looks at them
     assert append_call(lib, False, maxn=41, ks=NULL, vs=NULL) == pa.PA_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(P=16, to=NULL, NP=7), pa.PA_ERR_NULL_POINTER),
+    (dict(Hq=6, Hkv=4), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(k=FAKE + 8), pa.PA_ERR_ALIGNMENT),
+    (dict(scale=-1.0), pa.PA_ERR_BAD_VALUE),
+    (dict(S=0), pa.PA_OK),
+])
+def test_decode_xpacked_validation(lib, over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=4, Hkv=1, D=64, bs=16, nb=16,
+             mbps=7, scale=0.125, P=0, out=FAKE, ml=FAKE, es=FAKE, to=FAKE, NP=1)
+    a.update(over)
+    st = lib.paged_attn_decode_xpacked(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["S"], a["Hq"],
+                                       a["Hkv"], a["D"], a["bs"], a["nb"], a["mbps"], a["scale"],
+                                       a["P"], a["out"], a["ml"], a["es"], a["to"], a["NP"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kn=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(maxn=41), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=80), pa.PA_ERR_UNSUPPORTED),
+    (dict(vc=FAKE + 8), pa.PA_ERR_ALIGNMENT),
+    (dict(S=0), pa.PA_OK),
+])
+def test_kv_append_xpacked_validation(lib, over, status):
+    a = dict(kn=FAKE, vn=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, S=3, T=40, maxn=20, Hkv=8, D=128, bs=16,
+             nb=64, mbps=9, kc=FAKE, vc=FAKE)
+    a.update(over)
+    st = lib.paged_attn_kv_append_xpacked(a["kn"], a["vn"], a["bt"], a["sl"], a["cu"], a["S"], a["T"],
+                                          a["maxn"], a["Hkv"], a["D"], a["bs"], a["nb"], a["mbps"],
+                                          a["kc"], a["vc"], None)
+    assert st == status

@@ -221,3 +221,102 @@ def test_append_fp8_then_decode_fp8(orc):
     t.cuda.synchronize()
     assert np.array_equal(kc.cpu().numpy(), rk) and np.array_equal(vsd.cpu().numpy(), rvs)
     assert_out_close(bf16_host_f64(out), ref, "fp8 pipeline")
+
+
+# ---- the BI-V100 page's layouts: x-packed K, transposed V ------------------
+from tests.oracle_pins import to_xpacked  # noqa: E402
+
+
+@pytest.mark.parametrize("what,lens,n_new,Hkv,D", APPEND_CASES)
+def test_kv_append_xpacked_bit_exact(orc, what, lens, n_new, Hkv, D):
+    t = torch()
+    case, k_new, v_new, cu = append_problem("appendx", 503, lens, n_new, Hkv, D)
+    kx, vx = to_xpacked(case.k_cache, case.v_cache)
+    ref_k, ref_v = orc.kv_append_xpacked(k_new, v_new, case.block_tables, case.seq_lens, cu, kx, vx)
+    kd, vd = bf16_dev(kx), bf16_dev(vx)
+    announce(f"kv append x-packed: {what}")
+    pa.paged_attn_kv_append_xpacked(bf16_dev(k_new), bf16_dev(v_new), i32_dev(case.block_tables),
+                                    i32_dev(case.seq_lens), i32_dev(cu), int(max(n_new)), kd, vd)
+    t.cuda.synchronize()
+    assert np.array_equal(kd.cpu().view(t.int16).numpy().view(np.uint16), ref_k)
+    assert np.array_equal(vd.cpu().view(t.int16).numpy().view(np.uint16), ref_v)
+
+
+XP_CASES = [
+    ("tiny", lambda: workloads.tiny_decode(), (0, 16, 48)),
+    ("edges G=4 D=128", lambda: workloads.build_case("xpedges", 521, [1, 15, 16, 17, 511, 512, 513, 2000], 8, 2, 128), (0, 32, 512)),
+    ("G=6 D=256", lambda: workloads.build_case("xpd256", 522, [1, 100, 1030], 12, 2, 256), (0, 256)),
+    ("G=1 D=64", lambda: workloads.build_case("xpd64", 523, [3, 64, 700], 2, 2, 64), (0, 64)),
+    ("G=16 D=128", lambda: workloads.build_case("xpg16", 524, [900, 40, 1], 16, 1, 128), (0, 512)),
+    ("llama3-8b shape", lambda: workloads.llama3_8b_decode(), (512,)),
+]
+
+
+def run_decode_layouts(case, P):
+    """Decode (P = 0) or partials + merge through both layouts; returns
+    (row-major out, x-packed out, x-packed partials or None)."""
+    t = torch()
+    kx, vx = to_xpacked(case.k_cache, case.v_cache)
+    q, bt, sl = bf16_dev(case.q), i32_dev(case.block_tables), i32_dev(case.seq_lens)
+    k, v, kxd, vxd = bf16_dev(case.k_cache), bf16_dev(case.v_cache), bf16_dev(kx), bf16_dev(vx)
+    outs, parts = [], None
+    for xp in (False, True):
+        out = t.empty_like(q)
+        fn = pa.paged_attn_decode_xpacked if xp else pa.paged_attn_decode
+        kk, vv = (kxd, vxd) if xp else (k, v)
+        if P == 0:
+            fn(q, kk, vv, bt, sl, float(case.scale), 0, out=out)
+        else:
+            npart = pa.paged_attn_num_partitions(case.max_blocks_per_seq, 16, P)
+            ws = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
+            for b in (ws.max_logits, ws.exp_sums, ws.tmp_out):
+                b.fill_(float("nan"))
+            fn(q, kk, vv, bt, sl, float(case.scale), P, max_logits=ws.max_logits, exp_sums=ws.exp_sums,
+               tmp_out=ws.tmp_out, max_num_partitions=npart)
+            pa.paged_attn_decode_reduce(ws.max_logits, ws.exp_sums, ws.tmp_out, sl, P, out)
+            if xp:
+                parts = tuple(b.cpu().numpy().astype(np.float64) for b in (ws.max_logits, ws.exp_sums, ws.tmp_out))
+        t.cuda.synchronize()
+        outs.append(out)
+    return outs[0], outs[1], parts, kx, vx
+
+
+@pytest.mark.parametrize("what,make,partitions", XP_CASES)
+def test_decode_xpacked_parity(orc, what, make, partitions):
+    t = torch()
+    case = make()
+    ref = None
+    for P in partitions:
+        announce(f"x-packed decode {what}: P={P} S={case.num_seqs} Hq={case.num_q_heads} "
+                 f"Hkv={case.num_kv_heads} D={case.head_dim}")
+        o_rm, o_xp, parts, kx, vx = run_decode_layouts(case, P)
+        if ref is None:
+            ref = orc.decode_xpacked(case.q, kx, vx, case.block_tables, case.seq_lens, case.num_kv_heads,
+                                     case.scale)
+        assert_out_close(bf16_host_f64(o_xp), ref, f"x-packed {what} P={P}")
+        # the same operands reach the same MFMAs in both layouts
+        assert np.array_equal(o_rm.cpu().view(t.int16).numpy(), o_xp.cpu().view(t.int16).numpy()), \
+            f"x-packed {what} P={P}: not bit-identical to the row-major layout"
+        if parts is not None:
+            rml, res, rto = orc.decode_partials_xpacked(case.q, kx, vx, case.block_tables, case.seq_lens,
+                                                        case.num_kv_heads, case.scale, P, parts[0].shape[2])
+            assert_partials_close(*parts, rml, res, rto, case.seq_lens, P, f"x-packed {what} P={P}")
+
+
+def test_decode_xpacked_nan_in_unused_slots(orc):
+    """Slots past a sequence's end may hold NaN in either layout."""
+    t = torch()
+    case = workloads.build_case("xpnan", 525, [5, 16, 33, 100], 8, 2, 128)
+    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    for s, L in enumerate(case.seq_lens):
+        nb = (int(L) + 15) // 16
+        if L % 16:
+            b = case.block_tables[s, nb - 1]
+            kc[b, :, L % 16:] = 0x7FC0
+            vc[b, :, L % 16:] = 0x7FC0
+    case2 = workloads.PagedCase(**{**case.__dict__, "k_cache": kc, "v_cache": vc})
+    ref = orc.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, 2, case.scale)
+    announce("x-packed decode with NaN tails")
+    for P in (0, 32):
+        _, o_xp, _, _, _ = run_decode_layouts(case2, P)
+        assert_out_close(bf16_host_f64(o_xp), ref, f"x-packed NaN tails P={P}")
