@@ -194,6 +194,14 @@ def run_decode(args, pa):
                                                 c0.kv_tokens)
     devs = [to_device(c) for c in cases]
     fp8 = args.kv_dtype == "fp8"
+    xp = args.kv_layout == "xpacked"
+    if fp8 and xp:
+        raise SystemExit("--kv-layout xpacked holds bf16 values")
+    if xp:  # the same cache rearranged on the GPU (torch permute: plumbing, not the method)
+        for d in devs:
+            nb, hkv, bs, D = d["k"].shape
+            d["k"] = d["k"].view(nb, hkv, bs, D // 8, 8).permute(0, 1, 3, 2, 4).contiguous()
+            d["v"] = d["v"].permute(0, 1, 3, 2).contiguous()
     if fp8:
         t0 = time.perf_counter()
         devs = [to_fp8_cache(pa, c, d) for c, d in zip(cases, devs)]
@@ -213,6 +221,9 @@ def run_decode(args, pa):
         if fp8:
             pa.paged_attn_decode_fp8(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["bt"], d["sl"], scale,
                                      P, stream=stream, **kw)
+        elif xp:
+            pa.paged_attn_decode_xpacked(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
+                                         stream=stream, **kw)
         else:
             pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P, stream=stream, **kw)
     out = torch.empty_like(devs[0]["q"])
@@ -270,8 +281,8 @@ def run_decode(args, pa):
     kv_bytes = tokens * bytes_per_token
     step_gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     kern_gbps = kv_bytes / (ms_kernel * 1e-3) / 1e9
-    traffic = counter_traffic("decode_fp8" if fp8 else "decode", DECODE_SOURCE,
-                              args.workload)
+    traffic = counter_traffic("decode_fp8" if fp8 else "decode_xpacked" if xp else "decode",
+                              DECODE_SOURCE, args.workload)
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -286,8 +297,9 @@ def run_decode(args, pa):
         "dtype": "fp8-e4m3 kv, bf16 q" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": args.workload + ("_fp8" if fp8 else ""),
-            "kv_cache": "fp8 e4m3 + per-position fp32 scales" if fp8 else "bf16",
+            "workload": args.workload + ("_fp8" if fp8 else "") + ("_xpacked" if xp else ""),
+            "kv_cache": ("fp8 e4m3 + per-position fp32 scales" if fp8 else "bf16")
+                        + (", x-packed K / transposed V" if xp else ""),
             "num_seqs": c0.num_seqs,
             "num_q_heads": c0.num_q_heads,
             "num_kv_heads": c0.num_kv_heads,
@@ -306,7 +318,7 @@ def run_decode(args, pa):
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_decode_compact_kernel (fused merge)" if fused else "paged_decode_compact_kernel")
-                      + (" <FP8>" if fp8 else ""),
+                      + (" <FP8>" if fp8 else "") + (" <x-packed>" if xp else ""),
             "achieved": kern_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -464,6 +476,9 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_split_decode", "large_ragged_decode",
                              "ragged_prefill", "tiny_decode", "kv_append"])
+    ap.add_argument("--kv-layout", default="tile", choices=["tile", "xpacked"],
+                    help="decode workloads: row-major [blocks, H_kv, 16, D] tiles, or x-packed K "
+                         "[blocks, H_kv, D/8, 16, 8] with transposed V [blocks, H_kv, D, 16]")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="decode workloads and kv_append: bf16 cache, or FP8 (E4M3 codes with "
                          "per-position scales) quantized on the GPU by the library's append kernel")
@@ -501,7 +516,7 @@ def main():
         result, case = run_append(args, pa)
     else:
         result, case = run_decode(args, pa)
-    if not args.no_cpu_baseline and case is not None and args.kv_dtype == "bf16":
+    if not args.no_cpu_baseline and case is not None and args.kv_dtype == "bf16" and args.kv_layout == "tile":
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, args.workload == "ragged_prefill")
     else:
