@@ -25,6 +25,9 @@ Definitions followed (details in the C source):
                  page, "Stage D: FP8 Paged KV Gather" and "FP8 KV
                  Quantize/Dequant"): quantize_fp8, fp8_dequant, kv_append_fp8,
                  and decode / partials over the dequantized (fp64) cache.
+  tokens      -- the AstrAI page's token-granular cache (decode with
+                 page_size=1, kv_indptr + page indices): cache [num_slots, H_kv,
+                 D], sequence s's token t in slot kv_indices[kv_indptr[s] + t].
   xpacked     -- the BI-V100 page's cache layouts (section 3 "Paged K/V
                  Gather"): K [num_blocks, H_kv, D/8, bs, 8], V [num_blocks,
                  H_kv, D, bs]; decode, partials and append over them.
@@ -87,6 +90,10 @@ class Oracle:
         lib.oracle_kv_append_xpacked.argtypes = lib.oracle_kv_append.argtypes
         lib.oracle_decode_xpacked.argtypes = lib.oracle_decode.argtypes
         lib.oracle_decode_partials_xpacked.argtypes = lib.oracle_decode_partials.argtypes
+        lib.oracle_decode_tokens.argtypes = [_u16p, _u16p, _u16p, _i32p, _i32p] + [_c_int] * 4 + [
+            ctypes.c_float, _f64p]
+        lib.oracle_decode_partials_tokens.argtypes = [_u16p, _u16p, _u16p, _i32p, _i32p] + [_c_int] * 4 + [
+            ctypes.c_float, _c_int, _c_int, _f64p, _f64p, _f64p]
         lib.oracle_kv_append_fp8.argtypes = ([_u16p, _u16p, _i32p, _i32p, _i32p] + [_c_int] * 5 +
                                              [_u8p, _u8p, _f32p, _f32p])
         lib.oracle_quantize_fp8.argtypes = [_u16p, ctypes.c_long, _c_int, _u8p, _f32p]
@@ -97,7 +104,8 @@ class Oracle:
                    "oracle_mutant", "oracle_num_threads", "oracle_decode_f64kv",
                    "oracle_decode_partials_f64kv", "oracle_kv_append", "oracle_kv_append_fp8",
                    "oracle_quantize_fp8", "oracle_fp8_dequant", "oracle_kv_append_xpacked",
-                   "oracle_decode_xpacked", "oracle_decode_partials_xpacked"):
+                   "oracle_decode_xpacked", "oracle_decode_partials_xpacked",
+                   "oracle_decode_tokens", "oracle_decode_partials_tokens"):
             getattr(lib, fn).restype = ctypes.c_int
         self.lib = lib
 
@@ -256,6 +264,39 @@ class Oracle:
                                                      int(partition_size), NP, ml, es, to)
         if rc:
             raise ValueError(f"oracle_decode_partials_xpacked rejected the shapes (status {rc})")
+        return ml, es, to
+
+    # ---- O1 / O2 over a token-granular cache (page_size 1, kv_indptr) -------
+    def decode_tokens(self, q, k_cache, v_cache, kv_indptr, kv_indices, num_kv_heads: int,
+                      scale) -> np.ndarray:
+        """k_cache / v_cache [num_slots, H_kv, D] bf16 bits; sequence s's token t
+        is slot kv_indices[kv_indptr[s] + t]."""
+        q = self._c(q, np.uint16)
+        S, Hq, D = q.shape
+        out = np.empty((S, Hq, D), dtype=np.float64)
+        rc = self.lib.oracle_decode_tokens(q, self._c(k_cache, np.uint16), self._c(v_cache, np.uint16),
+                                           self._c(kv_indptr, np.int32), self._c(kv_indices, np.int32),
+                                           S, Hq, num_kv_heads, D, float(np.float32(scale)), out)
+        if rc:
+            raise ValueError(f"oracle_decode_tokens rejected the shapes (status {rc})")
+        return out
+
+    def decode_partials_tokens(self, q, k_cache, v_cache, kv_indptr, kv_indices, num_kv_heads: int,
+                               scale, partition_size: int, max_num_partitions: int):
+        q = self._c(q, np.uint16)
+        S, Hq, D = q.shape
+        NP = int(max_num_partitions)
+        ml = np.full((S, Hq, NP), np.nan)
+        es = np.full((S, Hq, NP), np.nan)
+        to = np.full((S, Hq, NP, D), np.nan)
+        rc = self.lib.oracle_decode_partials_tokens(q, self._c(k_cache, np.uint16),
+                                                    self._c(v_cache, np.uint16),
+                                                    self._c(kv_indptr, np.int32),
+                                                    self._c(kv_indices, np.int32), S, Hq,
+                                                    num_kv_heads, D, float(np.float32(scale)),
+                                                    int(partition_size), NP, ml, es, to)
+        if rc:
+            raise ValueError(f"oracle_decode_partials_tokens rejected the shapes (status {rc})")
         return ml, es, to
 
     def kv_append_xpacked(self, k_new, v_new, block_tables, seq_lens, cu_seqlens, k_cache, v_cache):

@@ -299,6 +299,70 @@ int oracle_decode_partials_xpacked(const uint16_t *q, const uint16_t *k_cache,
                          max_logits, exp_sums, tmp_out);
 }
 
+/* O1 and O2 over a token-granular cache (the AstrAI page's decode with
+ * page_size=1: "kv_indptr" gives each request's KV length, the page indices
+ * translate logical positions to physical slots).  Sequence s has
+ * L = kv_indptr[s+1] - kv_indptr[s] tokens; token t's K/V row of kv head g is
+ * cache[kv_indices[kv_indptr[s] + t], g, :] in a [num_slots, H_kv, D] cache,
+ * i.e. the block-table walk with one-token blocks whose table row is
+ * kv_indices + kv_indptr[s]. */
+static int tokens_L(const int32_t *kv_indptr, int s) {
+#if ORACLE_MUTANT == 20
+    return kv_indptr[s + 1]; /* the offset taken for the length */
+#else
+    return kv_indptr[s + 1] - kv_indptr[s];
+#endif
+}
+
+int oracle_decode_tokens(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                         const int32_t *kv_indptr, const int32_t *kv_indices, int S, int Hq,
+                         int Hkv, int D, float scale, double *out) {
+    if (Hq % Hkv != 0) return 2;
+    kv_cache_t k = {k_cache, NULL, 0, 1, D}, v = {v_cache, NULL, 0, 1, D};
+    long pairs = (long)S * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < pairs; ++i) {
+        int s = (int)(i / Hq), h = (int)(i % Hq);
+        int L = tokens_L(kv_indptr, s);
+        double *o = out + i * D;
+        if (L <= 0) { for (int d = 0; d < D; ++d) o[d] = 0.0; continue; }
+        double *z = (double *)malloc(sizeof(double) * (size_t)(L + 1));
+        double m, l;
+        attend_range(q_row(q, s, h, Hq, D, S), k, v, kv_indices + kv_indptr[s], 0,
+                     kv_head_of(h, Hq, Hkv), 0, L, Hkv, 1, D, L, (double)scale, z, o, &m, &l);
+        free(z);
+    }
+    return 0;
+}
+
+int oracle_decode_partials_tokens(const uint16_t *q, const uint16_t *k_cache,
+                                  const uint16_t *v_cache, const int32_t *kv_indptr,
+                                  const int32_t *kv_indices, int S, int Hq, int Hkv, int D,
+                                  float scale, int P, int NP, double *max_logits,
+                                  double *exp_sums, double *tmp_out) {
+    if (Hq % Hkv != 0 || P <= 0) return 2;
+    kv_cache_t k = {k_cache, NULL, 0, 1, D}, v = {v_cache, NULL, 0, 1, D};
+    long work = (long)S * Hq * NP;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < work; ++i) {
+        int p = (int)(i % NP);
+        long sh = i / NP;
+        int s = (int)(sh / Hq), h = (int)(sh % Hq);
+        int L = tokens_L(kv_indptr, s);
+        if (p >= (L + P - 1) / P) continue;
+        int t0 = p * P, t1 = (p + 1) * P < L ? (p + 1) * P : L;
+        double *z = (double *)malloc(sizeof(double) * (size_t)(t1 - t0 + 1));
+        double m, l;
+        attend_range(q_row(q, s, h, Hq, D, S), k, v, kv_indices + kv_indptr[s], 0,
+                     kv_head_of(h, Hq, Hkv), t0, t1, Hkv, 1, D, L, (double)scale, z,
+                     tmp_out + i * D, &m, &l);
+        max_logits[i] = m;
+        exp_sums[i] = l;
+        free(z);
+    }
+    return 0;
+}
+
 /* O3 -- cross-partition merge (BI-V100 design page, section 2 "combine" and
  * "Level 3: Cross-Partition Coordination"): with M = max_p m_p and weights
  * w_p = exp(m_p - M) * l_p, out = sum_p w_p * o_p / sum_p w_p over the

@@ -602,6 +602,66 @@ def pin_xpacked_append_refills_erased_rows(orc):
     assert np.array_equal(k2, kx) and np.array_equal(v2, vx), "x-packed append did not restore the cache"
 
 
+# --------------------------------------------------------------------------
+# token-granular cache (page_size 1, kv_indptr + kv_indices)
+# --------------------------------------------------------------------------
+def _tokens_problem(seed, Hq, Hkv, D, lens, extra=7):
+    """Contiguous K/V per sequence scattered by the test into a shuffled
+    [num_slots, H_kv, D] slot pool (unused slots hold poison)."""
+    rng = np.random.default_rng(seed)
+    kc = [rand_bits(rng, (L, Hkv, D)) for L in lens]
+    vc = [rand_bits(rng, (L, Hkv, D)) for L in lens]
+    q = rand_bits(rng, (len(lens), Hq, D))
+    total = sum(lens)
+    slots = total + extra
+    perm = rng.permutation(slots).astype(np.int32)
+    kpool = np.full((slots, Hkv, D), POISON_BITS, np.uint16)
+    vpool = np.full((slots, Hkv, D), POISON_BITS, np.uint16)
+    indptr = np.zeros(len(lens) + 1, np.int32)
+    indptr[1:] = np.cumsum(lens)
+    indices = perm[:total].copy()
+    for s, L in enumerate(lens):
+        idx = indices[indptr[s]:indptr[s + 1]]
+        kpool[idx] = kc[s]
+        vpool[idx] = vc[s]
+    return q, kc, vc, kpool, vpool, indptr, indices
+
+
+def pin_tokens_decode_brute_force(orc):
+    for seed, Hq, Hkv, D, lens in [(81, 4, 2, 16, [1, 5, 17, 40]), (82, 6, 3, 32, [70, 0, 9])]:
+        q, kc, vc, kpool, vpool, indptr, indices = _tokens_problem(seed, Hq, Hkv, D, lens)
+        scale = np.float32(1.0 / math.sqrt(D))
+        out = orc.decode_tokens(q, kpool, vpool, indptr, indices, Hkv, scale)
+        G = Hq // Hkv
+        for s, L in enumerate(lens):
+            if L == 0:
+                assert np.all(out[s] == 0.0)
+                continue
+            K, V = _f(kc[s]), _f(vc[s])
+            for h in range(Hq):
+                ref, _, _ = brute_attention(_f(q[s, h]), K, V, h // G, float(scale), L)
+                _close(out[s, h], ref, 1e-12, f"token-granular decode seed {seed} s{s} h{h}")
+
+
+def pin_tokens_equals_block_size_one(orc):
+    """A token-granular cache is a block cache with one-token blocks whose
+    table rows are the index lists: outputs and partials agree bit for bit."""
+    lens = [33, 1, 130, 64]
+    q, kc, vc, kpool, vpool, indptr, indices = _tokens_problem(83, 8, 2, 32, lens)
+    bt = np.zeros((len(lens), max(lens)), np.int32)
+    for s, L in enumerate(lens):
+        bt[s, :L] = indices[indptr[s]:indptr[s + 1]]
+    sl = np.asarray(lens, np.int32)
+    kb, vb = kpool[:, :, None, :], vpool[:, :, None, :]
+    scale = np.float32(0.2)
+    assert np.array_equal(orc.decode_tokens(q, kpool, vpool, indptr, indices, 2, scale),
+                          orc.decode(q, kb, vb, bt, sl, 2, scale))
+    a = orc.decode_partials_tokens(q, kpool, vpool, indptr, indices, 2, scale, 32, 5)
+    b = orc.decode_partials(q, kb, vb, bt, sl, 2, scale, 32, 5)
+    for u, w in zip(a, b):
+        assert np.array_equal(np.nan_to_num(u), np.nan_to_num(w))
+
+
 PINS: Dict[str, Callable] = {name: fn for name, fn in sorted(globals().items())
                              if name.startswith("pin_") and callable(fn)}
 

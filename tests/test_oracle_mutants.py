@@ -6,7 +6,8 @@ K used as V, a dropped denominator term, unnormalized partials, overlapping
 partitions, a merge without exp_sum weights, a dropped causal diagonal,
 top-left causal alignment, a shifted query row, a transposed query index,
 FP8 ties away from zero, a wrong FP8 scale, a late append position, FP8
-subnormals dropped, a swapped x-packed K index).
+subnormals dropped, a swapped x-packed K index, a token-granular length read
+as the end offset).
 Every build runs the pin suite in a child process (a mutant may crash); the
 test requires at least one failing pin or a crash for each.
 """
@@ -39,6 +40,7 @@ MUTANTS = {
     17: "append one position late",
     18: "FP8 subnormals read as zero",
     19: "x-packed K index with chunk and lane swapped",
+    20: "token-granular length read as the end offset",
 }
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
