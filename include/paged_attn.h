@@ -160,6 +160,38 @@ int paged_attn_decode_xpacked(const void *q, const void *k_cache, const void *v_
                               float *tmp_out, int max_num_partitions, void *stream);
 
 /*
+ * Paged GQA decode over a token-granular cache (the AstrAI page, "Attention
+ * Backend" and "Q Scheduling and KV Addressing": decode with page_size=1,
+ * kv_indptr giving each request's KV length, page indices translating logical
+ * positions to physical slots):
+ *   k_cache, v_cache  bf16 [num_slots, H_kv, D]
+ *   kv_indptr         int32 [num_seqs + 1], non-decreasing; sequence s has
+ *                     L = kv_indptr[s+1] - kv_indptr[s] tokens
+ *   kv_indices        int32 [kv_indptr[num_seqs]]; token t of sequence s is
+ *                     slot kv_indices[kv_indptr[s] + t]
+ * Same computation, outputs, partials and status codes as paged_attn_decode.
+ * max_kv_len (host) must be >= every L: it sizes the launch, and with
+ * partition_size > 0 max_num_partitions must be >= ceil(max_kv_len / P)
+ * rounded up to whole 16-token tiles, i.e. paged_attn_num_partitions(
+ * ceil(max_kv_len / 16), 16, P).  Merge the partials with
+ * paged_attn_decode_reduce_indptr.  Slot ids and offsets are device values,
+ * not checked.
+ */
+int paged_attn_decode_tokens(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *kv_indptr, const int32_t *kv_indices, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int head_dim, int num_slots,
+                             int max_kv_len, float scale, int partition_size, void *out,
+                             float *max_logits, float *exp_sums, float *tmp_out,
+                             int max_num_partitions, void *stream);
+
+/* paged_attn_decode_reduce with each sequence's length taken from adjacent
+ * kv_indptr entries (for the partials of paged_attn_decode_tokens). */
+int paged_attn_decode_reduce_indptr(const float *max_logits, const float *exp_sums,
+                                    const float *tmp_out, const int32_t *kv_indptr, int num_seqs,
+                                    int num_q_heads, int head_dim, int partition_size,
+                                    int max_num_partitions, void *out, void *stream);
+
+/*
  * KV append: writes the K/V rows of new tokens into their cache slots -- the
  * cache write before decode and prefill (the AstrAI page's backend layer "owns
  * KV cache writes and reads").  Sequence s owns rows [cu_seqlens[s],

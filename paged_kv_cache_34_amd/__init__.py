@@ -60,6 +60,8 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_kv_append_fp8.argtypes = [_vp] * 5 + [_i] * 8 + [_vp] * 5
         lib.paged_attn_decode_xpacked.argtypes = lib.paged_attn_decode.argtypes
         lib.paged_attn_kv_append_xpacked.argtypes = lib.paged_attn_kv_append.argtypes
+        lib.paged_attn_decode_tokens.argtypes = [_vp] * 5 + [_i] * 6 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp]
+        lib.paged_attn_decode_reduce_indptr.argtypes = lib.paged_attn_decode_reduce.argtypes
         lib.paged_attn_prefill_ragged.argtypes = [_vp] * 6 + [_i] * 9 + [ctypes.c_float, _vp, _vp]
         lib.paged_attn_prefill_ragged_split.argtypes = ([_vp] * 6 + [_i] * 9 + [ctypes.c_float, _i, _vp,
                                                           ctypes.c_longlong, _vp, _vp])
@@ -74,6 +76,7 @@ def library() -> ctypes.CDLL:
         for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
                    "paged_attn_decode_fp8", "paged_attn_kv_append", "paged_attn_kv_append_fp8",
                    "paged_attn_decode_xpacked", "paged_attn_kv_append_xpacked",
+                   "paged_attn_decode_tokens", "paged_attn_decode_reduce_indptr",
                    "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
                    "paged_attn_prefill_chunk_size",
                    "paged_attn_num_partitions", "paged_attn_choose_partition_size",
@@ -243,6 +246,47 @@ def paged_attn_decode_xpacked(q, k_cache, v_cache, block_tables, seq_lens, scale
         _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), int(max_num_partitions),
         _stream(stream))
     _check("paged_attn_decode_xpacked", st)
+
+
+def paged_attn_decode_tokens(q, k_cache, v_cache, kv_indptr, kv_indices, max_kv_len: int,
+                             scale: float, partition_size: int = 0, out=None, max_logits=None,
+                             exp_sums=None, tmp_out=None, max_num_partitions: Optional[int] = None,
+                             stream=None) -> None:
+    """Decode over a token-granular cache k/v [num_slots, H_kv, D]; sequence s's
+    token t is slot kv_indices[kv_indptr[s] + t]."""
+    import torch
+    _want(q, torch.bfloat16, "q")
+    _want(k_cache, torch.bfloat16, "k_cache")
+    _want(v_cache, torch.bfloat16, "v_cache")
+    _want(kv_indptr, torch.int32, "kv_indptr")
+    _want(kv_indices, torch.int32, "kv_indices")
+    _want(out, torch.bfloat16, "out")
+    for name, t in (("max_logits", max_logits), ("exp_sums", exp_sums), ("tmp_out", tmp_out)):
+        _want(t, torch.float32, name)
+    num_seqs, hq, d = q.shape
+    num_slots, hkv, _ = k_cache.shape
+    if max_num_partitions is None:
+        max_num_partitions = tmp_out.shape[2] if tmp_out is not None else 1
+    st = library().paged_attn_decode_tokens(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr), _ptr(kv_indices), num_seqs, hq, hkv,
+        d, num_slots, int(max_kv_len), float(scale), int(partition_size), _ptr(out), _ptr(max_logits),
+        _ptr(exp_sums), _ptr(tmp_out), int(max_num_partitions), _stream(stream))
+    _check("paged_attn_decode_tokens", st)
+
+
+def paged_attn_decode_reduce_indptr(max_logits, exp_sums, tmp_out, kv_indptr, partition_size: int,
+                                    out, stream=None) -> None:
+    """Merge partials [S, H_q, NP(, D)] with lengths from adjacent kv_indptr entries."""
+    import torch
+    for name, t in (("max_logits", max_logits), ("exp_sums", exp_sums), ("tmp_out", tmp_out)):
+        _want(t, torch.float32, name)
+    _want(kv_indptr, torch.int32, "kv_indptr")
+    _want(out, torch.bfloat16, "out")
+    s, hq, npart, d = tmp_out.shape
+    st = library().paged_attn_decode_reduce_indptr(
+        _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(kv_indptr), s, hq, d,
+        int(partition_size), npart, _ptr(out), _stream(stream))
+    _check("paged_attn_decode_reduce_indptr", st)
 
 
 def paged_attn_kv_append_xpacked(k_new, v_new, block_tables, seq_lens, cu_seqlens,

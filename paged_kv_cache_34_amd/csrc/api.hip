@@ -137,7 +137,8 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
                   int max_blocks_per_seq, float scale, int partition_size, void *out,
                   float *max_logits, float *exp_sums, float *tmp_out, int max_num_partitions,
                   int32_t *counters, void *stream, const float *k_scales = nullptr,
-                  const float *v_scales = nullptr, bool xpacked = false) {
+                  const float *v_scales = nullptr, bool xpacked = false,
+                  const int32_t *kv_indptr = nullptr) {
     int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
     if (st != PA_OK) return st;
@@ -180,8 +181,11 @@ int decode_common(const void *q, const void *k_cache, const void *v_cache,
     a.counters = counters;
     a.k_scales = k_scales;
     a.v_scales = v_scales;
+    a.kv_indptr = kv_indptr;
     a.stream = static_cast<hipStream_t>(stream);
-    const hipError_t e = fp8 ? pa::launch_decode_fp8(a) : xpacked ? pa::launch_decode_xpacked(a) : pa::launch_decode(a);
+    const hipError_t e = fp8 ? pa::launch_decode_fp8(a)
+                         : xpacked ? pa::launch_decode_xpacked(a)
+                         : kv_indptr ? pa::launch_decode_tokens(a) : pa::launch_decode(a);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -287,11 +291,13 @@ int paged_attn_decode_fused(const void *q, const void *k_cache, const void *v_ca
                          counters, stream);
 }
 
-int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
-                             const float *tmp_out, const int32_t *seq_lens, int num_seqs,
-                             int num_q_heads, int head_dim, int partition_size,
-                             int max_num_partitions, void *out, void *stream) {
-    if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !out) return PA_ERR_NULL_POINTER;
+namespace {
+int reduce_common(const float *max_logits, const float *exp_sums, const float *tmp_out,
+                  const int32_t *seq_lens, const int32_t *kv_indptr, int num_seqs, int num_q_heads,
+                  int head_dim, int partition_size, int max_num_partitions, void *out,
+                  void *stream) {
+    if (!max_logits || !exp_sums || !tmp_out || !(seq_lens || kv_indptr) || !out)
+        return PA_ERR_NULL_POINTER;
     if (num_seqs < 0 || num_q_heads <= 0 || partition_size <= 0 || max_num_partitions <= 0 ||
         partition_size % kBlockSize != 0)
         return PA_ERR_BAD_SHAPE;
@@ -304,6 +310,7 @@ int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
     a.exp_sums = exp_sums;
     a.tmp_out = tmp_out;
     a.seq_lens = seq_lens;
+    a.kv_indptr = kv_indptr;
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.head_dim = head_dim;
@@ -312,6 +319,25 @@ int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
     a.out = static_cast<uint16_t *>(out);
     a.stream = static_cast<hipStream_t>(stream);
     return pa::launch_reduce(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+}  // namespace
+
+int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
+                             const float *tmp_out, const int32_t *seq_lens, int num_seqs,
+                             int num_q_heads, int head_dim, int partition_size,
+                             int max_num_partitions, void *out, void *stream) {
+    if (!seq_lens) return PA_ERR_NULL_POINTER;
+    return reduce_common(max_logits, exp_sums, tmp_out, seq_lens, nullptr, num_seqs, num_q_heads,
+                         head_dim, partition_size, max_num_partitions, out, stream);
+}
+
+int paged_attn_decode_reduce_indptr(const float *max_logits, const float *exp_sums,
+                                    const float *tmp_out, const int32_t *kv_indptr, int num_seqs,
+                                    int num_q_heads, int head_dim, int partition_size,
+                                    int max_num_partitions, void *out, void *stream) {
+    if (!kv_indptr) return PA_ERR_NULL_POINTER;
+    return reduce_common(max_logits, exp_sums, tmp_out, nullptr, kv_indptr, num_seqs, num_q_heads,
+                         head_dim, partition_size, max_num_partitions, out, stream);
 }
 
 int paged_attn_prefill_ragged(const void *q, const void *k_cache, const void *v_cache,
@@ -470,6 +496,23 @@ int paged_attn_kv_append_xpacked(const void *k_new, const void *v_new, const int
     return append_common(k_new, v_new, block_tables, seq_lens, cu_seqlens, num_seqs, num_tokens,
                          max_new_tokens, num_kv_heads, head_dim, block_size, num_blocks,
                          max_blocks_per_seq, k_cache, v_cache, nullptr, nullptr, false, stream, true);
+}
+
+int paged_attn_decode_tokens(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *kv_indptr, const int32_t *kv_indices, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int head_dim, int num_slots,
+                             int max_kv_len, float scale, int partition_size, void *out,
+                             float *max_logits, float *exp_sums, float *tmp_out,
+                             int max_num_partitions, void *stream) {
+    if (!kv_indptr || !kv_indices) return PA_ERR_NULL_POINTER;
+    if (max_kv_len <= 0 || num_slots <= 0) return PA_ERR_BAD_SHAPE;
+    // one-token pages: the block walk with block_size 1 over the page indices,
+    // sized by max_kv_len (the partition count comes from it)
+    const int blocks = (max_kv_len + kBlockSize - 1) / kBlockSize;
+    return decode_common(q, k_cache, v_cache, kv_indices, kv_indptr, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, kBlockSize, num_slots, blocks, scale,
+                         partition_size, out, max_logits, exp_sums, tmp_out, max_num_partitions,
+                         nullptr, stream, nullptr, nullptr, false, kv_indptr);
 }
 
 }  // extern "C"

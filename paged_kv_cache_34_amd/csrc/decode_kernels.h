@@ -69,7 +69,19 @@ struct DecodeParams {
     // FP8 cache: dequant multipliers [num_blocks, H_kv, 16] (k_cache / v_cache
     // then hold E4M3 codes [num_blocks, H_kv, 16, D]); null for a bf16 cache
     const float *k_scales, *v_scales;
+    // token-granular cache (page size 1): K/V [num_slots, H_kv, D], sequence
+    // s's token t in slot block_tables[kv_indptr[s] + t] (block_tables then
+    // holds the page indices); null for a block cache
+    const int32_t *kv_indptr;
 };
+
+// Tokens of sequence `seq`: seq_lens, or adjacent kv_indptr entries.
+__device__ __forceinline__ int seq_len_of(const DecodeParams &prm, int seq) {
+    return prm.kv_indptr ? prm.kv_indptr[seq + 1] - prm.kv_indptr[seq] : prm.seq_lens[seq];
+}
+
+// Slot ids a wave stages in LDS per chunk of 64 tiles (token-granular cache).
+constexpr int kTokIdsPerWave = 64 * 16;
 
 // 16-byte words per lane of one ring slot: the K (or V) tile, plus, for an
 // FP8 cache, the dequant scales of the lane's 4 score tokens.
@@ -146,7 +158,7 @@ struct DecodeItem {
     int t_end, b_begin, my_nb, ids;
 };
 
-template <int NW>
+template <int NW, bool TOK = false>
 __device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq, int kvh, int part,
                                                 int L, int wave, int lane) {
     DecodeItem it;
@@ -162,7 +174,7 @@ __device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq
     const int nb = (it.t_end + kBlock - 1) / kBlock - it.b_begin;
     it.my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
     const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + it.b_begin + wave;
-    it.ids = (lane < min(64, it.my_nb)) ? bt_row[NW * lane] : 0;
+    it.ids = (!TOK && lane < min(64, it.my_nb)) ? bt_row[NW * lane] : 0;  // (token ids: staged in LDS)
     return it;
 }
 
@@ -195,14 +207,16 @@ __device__ __forceinline__ void lds_barrier() {
 //                  product keeps ~16 mantissa bits) -> lane holds dims
 //                  16 dt + 4 grp + i of head col.
 // Lanes with col >= G carry a copy of head 0; their results are never stored.
-template <int D, int G, int NW, int DEPTH, bool ONE_CHUNK, bool FP8, bool XP>
+template <int D, int G, int NW, int DEPTH, bool ONE_CHUNK, bool FP8, bool XP, bool TOK = false>
 __device__ __forceinline__ void decode_item(const DecodeParams &prm, const DecodeItem &it,
                                             const DecodeItem &nx, bool has_next, bool primed,
                                             u32x4 (&qb)[D / 32],
                                             u32x4 (&kbuf)[DEPTH + 1][KvWords<D, FP8>::N],
-                                            u32x4 (&vbuf)[DEPTH + 1][KvWords<D, FP8>::N], float *lds) {
+                                            u32x4 (&vbuf)[DEPTH + 1][KvWords<D, FP8>::N], float *lds,
+                                            int *tok_lds = nullptr) {
     using S = DecodeShape<D, G, NW>;
     static_assert(!(FP8 && XP), "the x-packed layout holds bf16");
+    static_assert(!(TOK && (FP8 || XP || ONE_CHUNK)), "the token-granular cache: bf16, grid launch");
     constexpr int NJ = S::NJ, NDT = S::NDT, VROW = S::VROW;
     constexpr int NW16 = KvWords<D, FP8>::N;      // words per ring slot
     // V tile loads: a token row is LPT lanes of 16 bytes (8 bf16 or 16 E4M3
@@ -277,7 +291,28 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     // empty descriptor, whose loads return zeros without touching memory.  All
     // choices are wave-uniform and the loads unconditional, so the compiler's
     // wait counts stay exact.
+    // Token-granular cache: per-lane row gathers.  The slot ids of the wave's
+    // chunk sit in LDS (stage_tok_ids); tiles past the chunk read slot 0 (they
+    // are prefetched but never computed), so every load stays in bounds.
+    int *my_ids = TOK ? tok_lds + wave * kTokIdsPerWave : nullptr;
+    auto load_tile_tok = [&](int j, int n, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
+        const bool cur = j < n;
+        const long row_stride = (long)prm.num_kv_heads * D;  // elements per slot
+        const long sk = cur ? my_ids[j * kBlock + col] : 0;
+        const uint16_t *kp = prm.k_cache + sk * row_stride + kvh * D + (grp * 8);
+#pragma unroll
+        for (int j2 = 0; j2 < NK; ++j2) kr[j2] = load_u32x4(kp + j2 * 32);
+#pragma unroll
+        for (int j2 = 0; j2 < NV; ++j2) {
+            const long sv = cur ? my_ids[j * kBlock + vrow + j2 * TPI] : 0;
+            vr[j2] = load_u32x4(prm.v_cache + sv * row_stride + kvh * D + vcol * 8);
+        }
+    };
     auto load_tile = [&](int ids, int j, int n, bool last, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
+        if constexpr (TOK) {
+            load_tile_tok(j, n, kr, vr);
+            return;
+        }
         const int base = (n + DEPTH) / (DEPTH + 1) * (DEPTH + 1);
         const int jn = j - base;
         const bool cur = j < n;
@@ -408,6 +443,20 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         }
     };
 
+    // token-granular cache: the slot ids of the wave's tiles c0 .. c0 + n - 1
+    // (16 per tile; tokens past the end get slot 0) into the wave's LDS region
+    auto stage_tok_ids = [&](int c0, int n) {
+        if constexpr (TOK) {
+            if (lane < n) {
+                const int tok0 = (b_begin + wave + NW * (c0 + lane)) * kBlock;
+                const int32_t *idx = prm.block_tables + prm.kv_indptr[seq];
+#pragma unroll
+                for (int k = 0; k < kBlock; ++k) my_ids[lane * kBlock + k] = (tok0 + k < t_end) ? idx[tok0 + k] : 0;
+            }
+            wave_lds_sync();
+        }
+    };
+    if (TOK) stage_tok_ids(0, min(64, my_nb));
     if (!primed) {
         load_q(seq, kvh);
 #pragma unroll
@@ -433,8 +482,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         for (int c0 = 0; c0 < my_nb; c0 += 64) {
             const int n = min(64, my_nb - c0);
             const bool last = c0 + 64 >= my_nb;
-            const int ids = c0 == 0 ? it.ids : ((lane < n) ? bt_row[NW * (c0 + lane)] : 0);
+            const int ids = (TOK || c0 == 0) ? it.ids : ((lane < n) ? bt_row[NW * (c0 + lane)] : 0);
             if (c0 > 0) {
+                if (TOK) stage_tok_ids(c0, n);
 #pragma unroll
                 for (int d = 0; d < DEPTH; ++d) load_tile(ids, d, n, last, kbuf[d], vbuf[d]);
             }
@@ -619,12 +669,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
 
 // One workgroup per (partition, kv head, sequence); workgroups whose partition
 // starts past the sequence end exit at once.
-template <int D, int G, int NW, int DEPTH, bool FP8, bool XP>
+template <int D, int G, int NW, int DEPTH, bool FP8, bool XP, bool TOK = false>
 __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams prm) {
     using S = DecodeShape<D, G, NW>;
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    __shared__ __attribute__((aligned(16))) int tok_ids[TOK ? NW * kTokIdsPerWave : 1];
     const int seq = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
-    const int L = prm.seq_lens[seq];
+    const int L = seq_len_of(prm, seq);
     const int P = prm.partition_size;
     if ((P ? part * P : 0) >= L) {
         if (P == 0) {  // empty sequence, single pass: zeros
@@ -634,9 +685,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
         return;
     }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const DecodeItem it = make_item<NW>(prm, seq, kvh, part, L, wave, threadIdx.x & 63);
+    const DecodeItem it = make_item<NW, TOK>(prm, seq, kvh, part, L, wave, threadIdx.x & 63);
     u32x4 qb[D / 32], kbuf[DEPTH + 1][KvWords<D, FP8>::N], vbuf[DEPTH + 1][KvWords<D, FP8>::N];
-    decode_item<D, G, NW, DEPTH, false, FP8, XP>(prm, it, it, false, false, qb, kbuf, vbuf, lds);
+    decode_item<D, G, NW, DEPTH, false, FP8, XP, TOK>(prm, it, it, false, false, qb, kbuf, vbuf, lds, tok_ids);
 }
 
 // Compact persistent split-KV: every workgroup first builds, in LDS, the
@@ -742,8 +793,9 @@ constexpr int kReduceUnroll = 4;   // partitions in flight per slot
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
     const float *__restrict__ max_logits, const float *__restrict__ exp_sums,
-    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens, int num_q_heads,
-    int head_dim, int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
+    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ kv_indptr, int num_q_heads, int head_dim, int partition_size,
+    int max_num_partitions, uint16_t *__restrict__ out) {
     constexpr int LPP = kReduceChunk / 4;  // lanes per partition row
     constexpr int SLOTS = NW * 64 / LPP;
     __shared__ __attribute__((aligned(16))) float red[SLOTS * kReduceChunk];
@@ -766,7 +818,7 @@ __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
     const bool speculate = max_num_partitions <= SLOTS;
     int n = 0;
     if (!speculate) {
-        const int L = seq_lens[seq];
+        const int L = kv_indptr ? kv_indptr[seq + 1] - kv_indptr[seq] : seq_lens[seq];
         n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
     }
     const int first_bound = speculate ? max_num_partitions : n;
@@ -781,7 +833,7 @@ __global__ __launch_bounds__(NW * 64) void paged_reduce_kernel(
         v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * head_dim) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (speculate) {
-        const int L = seq_lens[seq];
+        const int L = kv_indptr ? kv_indptr[seq + 1] - kv_indptr[seq] : seq_lens[seq];
         n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
     }
     uint16_t *o = out + row * head_dim + chunk * kReduceChunk;
@@ -857,8 +909,9 @@ constexpr int kWaveReduceMaxRounds = 8;  // slots per row beyond this use paged_
 template <int D>
 __global__ __launch_bounds__(256) void paged_reduce_wave_kernel(
     const float *__restrict__ max_logits, const float *__restrict__ exp_sums,
-    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens, int num_seqs,
-    int num_q_heads, int partition_size, int max_num_partitions, uint16_t *__restrict__ out) {
+    const float *__restrict__ tmp_out, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ kv_indptr, int num_seqs, int num_q_heads, int partition_size,
+    int max_num_partitions, uint16_t *__restrict__ out) {
     constexpr int LPR = D / 4;   // lanes per row
     constexpr int R = 64 / LPR;  // rows per wave
     constexpr int U = kWaveReduceUnroll;
@@ -873,7 +926,7 @@ __global__ __launch_bounds__(256) void paged_reduce_wave_kernel(
     const bool speculate = max_num_partitions <= R * U;
     int n = 0;
     if (!speculate) {
-        const int L = seq_lens[seq];
+        const int L = kv_indptr ? kv_indptr[seq + 1] - kv_indptr[seq] : seq_lens[seq];
         n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
     }
     const int first_bound = speculate ? max_num_partitions : n;
@@ -888,7 +941,7 @@ __global__ __launch_bounds__(256) void paged_reduce_wave_kernel(
         v[u] = in ? *reinterpret_cast<const f32x4 *>(base + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (speculate) {
-        const int L = seq_lens[seq];
+        const int L = kv_indptr ? kv_indptr[seq + 1] - kv_indptr[seq] : seq_lens[seq];
         n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
     }
     uint16_t *o = out + pair * D + d0;
@@ -978,15 +1031,16 @@ inline int cu_count() {
     return cached[dev];
 }
 
-template <int D, int G, bool FP8, bool XP>
+template <int D, int G, bool FP8, bool XP, bool TOK>
 hipError_t launch_decode_dg(const DecodeArgs &a) {
     constexpr int DEPTH = decode_depth(D, FP8);
     DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
                      a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2,
                      a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
-                     a.tmp_out, a.counters, a.k_scales, a.v_scales};
+                     a.tmp_out, a.counters, a.k_scales, a.v_scales, a.kv_indptr};
     dim3 block(kDecodeWaves * 64);
-    if (a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock && a.num_seqs <= kCompactMaxSeqs) {
+    if (!TOK && a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock &&
+        a.num_seqs <= kCompactMaxSeqs) {
         static int per_cu = 0;  // resident workgroups per CU for this instantiation
         if (per_cu == 0) {
             int n = 0;
@@ -1002,44 +1056,45 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
                            a.stream, prm);
     } else {
         dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-        hipLaunchKernelGGL((paged_decode_grid_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP>), grid, block, 0,
+        hipLaunchKernelGGL((paged_decode_grid_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP, TOK>), grid, block, 0,
                            a.stream, prm);
     }
     return hipGetLastError();
 }
 
-template <int D, bool FP8, bool XP>
+template <int D, bool FP8, bool XP, bool TOK>
 hipError_t launch_decode_d(const DecodeArgs &a, int G) {
     switch (G) {
-        case 1: return launch_decode_dg<D, 1, FP8, XP>(a);
-        case 2: return launch_decode_dg<D, 2, FP8, XP>(a);
-        case 3: return launch_decode_dg<D, 3, FP8, XP>(a);
-        case 4: return launch_decode_dg<D, 4, FP8, XP>(a);
-        case 5: return launch_decode_dg<D, 5, FP8, XP>(a);
-        case 6: return launch_decode_dg<D, 6, FP8, XP>(a);
-        case 7: return launch_decode_dg<D, 7, FP8, XP>(a);
-        case 8: return launch_decode_dg<D, 8, FP8, XP>(a);
-        case 9: return launch_decode_dg<D, 9, FP8, XP>(a);
-        case 10: return launch_decode_dg<D, 10, FP8, XP>(a);
-        case 11: return launch_decode_dg<D, 11, FP8, XP>(a);
-        case 12: return launch_decode_dg<D, 12, FP8, XP>(a);
-        case 13: return launch_decode_dg<D, 13, FP8, XP>(a);
-        case 14: return launch_decode_dg<D, 14, FP8, XP>(a);
-        case 15: return launch_decode_dg<D, 15, FP8, XP>(a);
-        case 16: return launch_decode_dg<D, 16, FP8, XP>(a);
+        case 1: return launch_decode_dg<D, 1, FP8, XP, TOK>(a);
+        case 2: return launch_decode_dg<D, 2, FP8, XP, TOK>(a);
+        case 3: return launch_decode_dg<D, 3, FP8, XP, TOK>(a);
+        case 4: return launch_decode_dg<D, 4, FP8, XP, TOK>(a);
+        case 5: return launch_decode_dg<D, 5, FP8, XP, TOK>(a);
+        case 6: return launch_decode_dg<D, 6, FP8, XP, TOK>(a);
+        case 7: return launch_decode_dg<D, 7, FP8, XP, TOK>(a);
+        case 8: return launch_decode_dg<D, 8, FP8, XP, TOK>(a);
+        case 9: return launch_decode_dg<D, 9, FP8, XP, TOK>(a);
+        case 10: return launch_decode_dg<D, 10, FP8, XP, TOK>(a);
+        case 11: return launch_decode_dg<D, 11, FP8, XP, TOK>(a);
+        case 12: return launch_decode_dg<D, 12, FP8, XP, TOK>(a);
+        case 13: return launch_decode_dg<D, 13, FP8, XP, TOK>(a);
+        case 14: return launch_decode_dg<D, 14, FP8, XP, TOK>(a);
+        case 15: return launch_decode_dg<D, 15, FP8, XP, TOK>(a);
+        case 16: return launch_decode_dg<D, 16, FP8, XP, TOK>(a);
         default: return hipErrorInvalidValue;
     }
 }
 
 // Decode launch for a bf16 (FP8 false) or FP8 cache, in the row-major tile
-// layout or (XP) the x-packed K / transposed V layout.
-template <bool FP8, bool XP>
+// layout, (XP) the x-packed K / transposed V layout, or (TOK) a
+// token-granular cache addressed through kv_indptr and page indices.
+template <bool FP8, bool XP, bool TOK = false>
 hipError_t launch_decode_t(const DecodeArgs &a) {
     const int G = a.num_q_heads / a.num_kv_heads;
     switch (a.head_dim) {
-        case 64: return launch_decode_d<64, FP8, XP>(a, G);
-        case 128: return launch_decode_d<128, FP8, XP>(a, G);
-        case 256: return launch_decode_d<256, FP8, XP>(a, G);
+        case 64: return launch_decode_d<64, FP8, XP, TOK>(a, G);
+        case 128: return launch_decode_d<128, FP8, XP, TOK>(a, G);
+        case 256: return launch_decode_d<256, FP8, XP, TOK>(a, G);
         default: return hipErrorInvalidValue;
     }
 }

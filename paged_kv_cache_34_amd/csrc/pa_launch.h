@@ -25,12 +25,16 @@ struct DecodeArgs {
     // FP8 cache: k_cache / v_cache hold E4M3 codes and these the per-position
     // dequant scales [num_blocks, H_kv, block_size]; null for a bf16 cache
     const float *k_scales = nullptr, *v_scales = nullptr;
+    // token-granular cache: block_tables holds the page indices, kv_indptr
+    // [num_seqs + 1] the per-sequence offsets into them; null otherwise
+    const int32_t *kv_indptr = nullptr;
     hipStream_t stream;
 };
 
 struct ReduceArgs {
     const float *max_logits, *exp_sums, *tmp_out;
     const int32_t *seq_lens;
+    const int32_t *kv_indptr = nullptr;  // lengths from adjacent entries instead of seq_lens
     int num_seqs, num_q_heads, head_dim, partition_size, max_num_partitions;
     uint16_t *out;
     hipStream_t stream;
@@ -75,6 +79,7 @@ struct AppendArgs {
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_decode_fp8(const DecodeArgs &a);
 hipError_t launch_decode_xpacked(const DecodeArgs &a);
+hipError_t launch_decode_tokens(const DecodeArgs &a);
 hipError_t launch_reduce(const ReduceArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
 hipError_t launch_kv_append(const AppendArgs &a);

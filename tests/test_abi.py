@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_num_partitions", "paged_attn_choose_partition_size",
         "paged_attn_prefill_tile_map", "paged_attn_status_string", "paged_attn_decode_fp8",
         "paged_attn_kv_append", "paged_attn_kv_append_fp8", "paged_attn_decode_xpacked",
-        "paged_attn_kv_append_xpacked"} | (
+        "paged_attn_kv_append_xpacked", "paged_attn_decode_tokens",
+        "paged_attn_decode_reduce_indptr"} | (
         set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
     for name in names:
         assert hasattr(lib, name), name
@@ -349,3 +350,34 @@ def test_kv_append_xpacked_validation(lib, over, status):
                                           a["maxn"], a["Hkv"], a["D"], a["bs"], a["nb"], a["mbps"],
                                           a["kc"], a["vc"], None)
     assert st == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ip=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(ix=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(q=NULL), pa.PA_ERR_NULL_POINTER),
+    (dict(maxkv=0), pa.PA_ERR_BAD_SHAPE),
+    (dict(slots=0), pa.PA_ERR_BAD_SHAPE),
+    (dict(P=32, NP=3), pa.PA_ERR_BAD_SHAPE),   # ceil(100 / 16) tiles of 16 -> 4 partitions of 32
+    (dict(Hq=6, Hkv=4), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(k=FAKE + 2), pa.PA_ERR_ALIGNMENT),
+    (dict(scale=0.0), pa.PA_ERR_BAD_VALUE),
+    (dict(S=0), pa.PA_OK),
+])
+def test_decode_tokens_validation(lib, over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ip=FAKE, ix=FAKE, S=2, Hq=4, Hkv=1, D=64, slots=300, maxkv=100,
+             scale=0.125, P=0, out=FAKE, ml=FAKE, es=FAKE, to=FAKE, NP=1)
+    a.update(over)
+    st = lib.paged_attn_decode_tokens(a["q"], a["k"], a["v"], a["ip"], a["ix"], a["S"], a["Hq"],
+                                      a["Hkv"], a["D"], a["slots"], a["maxkv"], a["scale"], a["P"],
+                                      a["out"], a["ml"], a["es"], a["to"], a["NP"], None)
+    assert st == status
+
+
+def test_reduce_indptr_validation(lib):
+    st = lib.paged_attn_decode_reduce_indptr(FAKE, FAKE, FAKE, None, 2, 4, 64, 16, 7, FAKE, None)
+    assert st == pa.PA_ERR_NULL_POINTER
+    st = lib.paged_attn_decode_reduce_indptr(FAKE, FAKE, FAKE, FAKE, 2, 4, 80, 16, 7, FAKE, None)
+    assert st == pa.PA_ERR_UNSUPPORTED
+    assert lib.paged_attn_decode_reduce_indptr(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, 16, 7, FAKE, None) == pa.PA_OK

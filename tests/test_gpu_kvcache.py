@@ -320,3 +320,105 @@ def test_decode_xpacked_nan_in_unused_slots(orc):
     for P in (0, 32):
         _, o_xp, _, _, _ = run_decode_layouts(case2, P)
         assert_out_close(bf16_host_f64(o_xp), ref, f"x-packed NaN tails P={P}")
+
+
+# ---- the AstrAI page's token-granular cache (page size 1, kv_indptr) -------
+def tokens_case(seed, lens, Hq, Hkv, D, extra=50):
+    """A [num_slots, H_kv, D] pool with each sequence's tokens in random slots
+    (unused slots hold NaN), kv_indptr and kv_indices, and bf16 N(0,1) data."""
+    rng = np.random.default_rng(seed)
+    total = int(sum(lens))
+    slots = total + extra
+    pool_k = workloads.f32_to_bf16_bits(rng.standard_normal((slots, Hkv, D)).astype(np.float32))
+    pool_v = workloads.f32_to_bf16_bits(rng.standard_normal((slots, Hkv, D)).astype(np.float32))
+    perm = rng.permutation(slots).astype(np.int32)
+    indptr = np.zeros(len(lens) + 1, np.int32)
+    indptr[1:] = np.cumsum(lens)
+    indices = perm[:total].copy()
+    unused = perm[total:]
+    pool_k[unused] = 0x7FC0
+    pool_v[unused] = 0x7FC0
+    q = workloads.f32_to_bf16_bits(rng.standard_normal((len(lens), Hq, D)).astype(np.float32))
+    return q, pool_k, pool_v, indptr, indices, np.float32(1.0 / math.sqrt(D))
+
+
+TOK_CASES = [
+    ("edges G=4 D=128", [1, 15, 16, 17, 511, 512, 513, 2000], 8, 2, 128, (0, 32, 512)),
+    ("G=6 D=256", [1, 100, 1030], 12, 2, 256, (0, 256)),
+    ("G=1 D=64, a zero length", [3, 0, 64, 700], 2, 2, 64, (0, 64)),
+    ("G=8 D=128, many chunks", [5000, 40], 16, 2, 128, (0, 1024)),
+]
+
+
+@pytest.mark.parametrize("what,lens,Hq,Hkv,D,partitions", TOK_CASES)
+def test_decode_tokens_parity(orc, what, lens, Hq, Hkv, D, partitions):
+    t = torch()
+    q, kp, vp, indptr, indices, scale = tokens_case(531, lens, Hq, Hkv, D)
+    ref = orc.decode_tokens(q, kp, vp, indptr, indices, Hkv, scale)
+    qd, kd, vd = bf16_dev(q), bf16_dev(kp), bf16_dev(vp)
+    ipd, ixd = i32_dev(indptr), i32_dev(indices if indices.size else np.zeros(1, np.int32))
+    max_kv = max(max(lens), 1)
+    for P in partitions:
+        announce(f"token-granular decode {what}: P={P} S={len(lens)} Hq={Hq} Hkv={Hkv} D={D}")
+        out = t.full_like(qd, float("nan"))
+        if P == 0:
+            pa.paged_attn_decode_tokens(qd, kd, vd, ipd, ixd, max_kv, float(scale), 0, out=out)
+            t.cuda.synchronize()
+            assert_out_close(bf16_host_f64(out), ref, f"tokens {what} single pass")
+            continue
+        npart = pa.paged_attn_num_partitions((max_kv + 15) // 16, 16, P)
+        ws = pa.DecodeWorkspace(len(lens), Hq, D, npart, "cuda")
+        for b in (ws.max_logits, ws.exp_sums, ws.tmp_out):
+            b.fill_(float("nan"))
+        pa.paged_attn_decode_tokens(qd, kd, vd, ipd, ixd, max_kv, float(scale), P,
+                                    max_logits=ws.max_logits, exp_sums=ws.exp_sums, tmp_out=ws.tmp_out,
+                                    max_num_partitions=npart)
+        pa.paged_attn_decode_reduce_indptr(ws.max_logits, ws.exp_sums, ws.tmp_out, ipd, P, out)
+        t.cuda.synchronize()
+        rml, res, rto = orc.decode_partials_tokens(q, kp, vp, indptr, indices, Hkv, scale, P, npart)
+        assert_partials_close(ws.max_logits.cpu().numpy().astype(np.float64),
+                              ws.exp_sums.cpu().numpy().astype(np.float64),
+                              ws.tmp_out.cpu().numpy().astype(np.float64), rml, res, rto,
+                              np.diff(indptr), P, f"tokens {what} P={P}")
+        assert_out_close(bf16_host_f64(out), ref, f"tokens {what} merged P={P}")
+
+
+def test_decode_tokens_equals_block_cache_one_kv_head():
+    """With one kv head a block cache [blocks, 1, 16, D] is the slot pool
+    [blocks * 16, 1, D]: the token-granular decode over slot ids
+    16 * block + slot equals the block decode bit for bit."""
+    t = torch()
+    case = workloads.build_case("tokblk", 532, [1, 40, 300, 1100], 8, 1, 128)
+    dev = Dev(case)
+    idx, indptr = [], [0]
+    for s, L in enumerate(case.seq_lens):
+        for tok in range(int(L)):
+            idx.append(int(case.block_tables[s, tok // 16]) * 16 + tok % 16)
+        indptr.append(len(idx))
+    nb = case.num_blocks
+    kp = dev.k.view(nb * 16, 1, case.head_dim)
+    vp = dev.v.view(nb * 16, 1, case.head_dim)
+    announce("token-granular decode vs block decode, one kv head")
+    for P in (0, 256):
+        a, b = t.empty_like(dev.q), t.empty_like(dev.q)
+        if P == 0:
+            pa.paged_attn_decode(dev.q, dev.k, dev.v, dev.bt, dev.sl, float(case.scale), 0, out=a)
+            pa.paged_attn_decode_tokens(dev.q, kp, vp, i32_dev(np.array(indptr, np.int32)),
+                                        i32_dev(np.array(idx, np.int32)), int(case.seq_lens.max()),
+                                        float(case.scale), 0, out=b)
+        else:
+            npart = pa.paged_attn_num_partitions(case.max_blocks_per_seq, 16, P)
+            w1 = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
+            w2 = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
+            pa.paged_attn_decode(dev.q, dev.k, dev.v, dev.bt, dev.sl, float(case.scale), P,
+                                 max_logits=w1.max_logits, exp_sums=w1.exp_sums, tmp_out=w1.tmp_out,
+                                 max_num_partitions=npart)
+            pa.paged_attn_decode_reduce(w1.max_logits, w1.exp_sums, w1.tmp_out, dev.sl, P, a)
+            ipd = i32_dev(np.array(indptr, np.int32))
+            pa.paged_attn_decode_tokens(dev.q, kp, vp, ipd, i32_dev(np.array(idx, np.int32)),
+                                        case.max_blocks_per_seq * 16, float(case.scale), P,
+                                        max_logits=w2.max_logits, exp_sums=w2.exp_sums, tmp_out=w2.tmp_out,
+                                        max_num_partitions=npart)
+            pa.paged_attn_decode_reduce_indptr(w2.max_logits, w2.exp_sums, w2.tmp_out, ipd, P, b)
+        t.cuda.synchronize()
+        assert np.array_equal(a.cpu().view(t.int16).numpy(), b.cpu().view(t.int16).numpy()), f"P={P}"
