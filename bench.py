@@ -195,8 +195,21 @@ def run_decode(args, pa):
     devs = [to_device(c) for c in cases]
     fp8 = args.kv_dtype == "fp8"
     xp = args.kv_layout == "xpacked"
-    if fp8 and xp:
-        raise SystemExit("--kv-layout xpacked holds bf16 values")
+    tok = args.kv_layout == "tokens"
+    if fp8 and (xp or tok):
+        raise SystemExit("--kv-layout xpacked / tokens hold bf16 values")
+    if tok:  # one-token pages: the same blocks' tokens as slots 16 * block + slot (torch: plumbing)
+        import numpy as np
+        for c, d in zip(cases, devs):
+            nb, hkv, bs, D = d["k"].shape
+            d["k"] = d["k"].permute(0, 2, 1, 3).contiguous().view(nb * bs, hkv, D)
+            d["v"] = d["v"].permute(0, 2, 1, 3).contiguous().view(nb * bs, hkv, D)
+            idx = [int(c.block_tables[s, t // bs]) * bs + t % bs
+                   for s, L in enumerate(c.seq_lens) for t in range(int(L))]
+            ip = np.zeros(c.num_seqs + 1, np.int32)
+            ip[1:] = np.cumsum(c.seq_lens)
+            d["indptr"] = torch.from_numpy(ip).cuda()
+            d["indices"] = torch.from_numpy(np.asarray(idx, np.int32)).cuda()
     if xp:  # the same cache rearranged on the GPU (torch permute: plumbing, not the method)
         for d in devs:
             nb, hkv, bs, D = d["k"].shape
@@ -224,6 +237,10 @@ def run_decode(args, pa):
         elif xp:
             pa.paged_attn_decode_xpacked(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P,
                                          stream=stream, **kw)
+        elif tok:
+            pa.paged_attn_decode_tokens(d["q"], d["k"], d["v"], d["indptr"], d["indices"],
+                                        c0.max_blocks_per_seq * c0.block_size, scale, P,
+                                        stream=stream, **kw)
         else:
             pa.paged_attn_decode(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P, stream=stream, **kw)
     out = torch.empty_like(devs[0]["q"])
@@ -238,7 +255,10 @@ def run_decode(args, pa):
                                        stream=stream)
             return
         decode_call(d, out)
-        if P:
+        if P and tok:
+            pa.paged_attn_decode_reduce_indptr(ws.max_logits, ws.exp_sums, ws.tmp_out, d["indptr"], P,
+                                               out, stream=stream)
+        elif P:
             pa.paged_attn_decode_reduce(ws.max_logits, ws.exp_sums, ws.tmp_out, d["sl"], P, out,
                                         stream=stream)
 
@@ -297,9 +317,11 @@ def run_decode(args, pa):
         "dtype": "fp8-e4m3 kv, bf16 q" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": args.workload + ("_fp8" if fp8 else "") + ("_xpacked" if xp else ""),
+            "workload": args.workload + ("_fp8" if fp8 else "") + ("_xpacked" if xp else "")
+                        + ("_tokens" if tok else ""),
             "kv_cache": ("fp8 e4m3 + per-position fp32 scales" if fp8 else "bf16")
-                        + (", x-packed K / transposed V" if xp else ""),
+                        + (", x-packed K / transposed V" if xp else "")
+                        + (", one-token pages (kv_indptr + page indices)" if tok else ""),
             "num_seqs": c0.num_seqs,
             "num_q_heads": c0.num_q_heads,
             "num_kv_heads": c0.num_kv_heads,
@@ -318,7 +340,8 @@ def run_decode(args, pa):
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_decode_compact_kernel (fused merge)" if fused else "paged_decode_compact_kernel")
-                      + (" <FP8>" if fp8 else "") + (" <x-packed>" if xp else ""),
+                      + (" <FP8>" if fp8 else "") + (" <x-packed>" if xp else "")
+                      + (" <token-granular, grid launch>" if tok else ""),
             "achieved": kern_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -476,9 +499,10 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_split_decode", "large_ragged_decode",
                              "ragged_prefill", "tiny_decode", "kv_append"])
-    ap.add_argument("--kv-layout", default="tile", choices=["tile", "xpacked"],
-                    help="decode workloads: row-major [blocks, H_kv, 16, D] tiles, or x-packed K "
-                         "[blocks, H_kv, D/8, 16, 8] with transposed V [blocks, H_kv, D, 16]")
+    ap.add_argument("--kv-layout", default="tile", choices=["tile", "xpacked", "tokens"],
+                    help="decode workloads: row-major [blocks, H_kv, 16, D] tiles, x-packed K "
+                         "[blocks, H_kv, D/8, 16, 8] with transposed V [blocks, H_kv, D, 16], or "
+                         "one-token pages [slots, H_kv, D] addressed by kv_indptr + page indices")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="decode workloads and kv_append: bf16 cache, or FP8 (E4M3 codes with "
                          "per-position scales) quantized on the GPU by the library's append kernel")
