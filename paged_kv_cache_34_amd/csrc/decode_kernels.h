@@ -690,12 +690,20 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
     decode_item<D, G, NW, DEPTH, false, FP8, XP, TOK>(prm, it, it, false, false, qb, kbuf, vbuf, lds, tok_ids);
 }
 
-// Compact persistent split-KV: every workgroup first builds, in LDS, the
-// prefix over sequences of their item counts H_kv * ceil(L / P) (items are
-// ordered sequence, kv head, partition), then takes items blockIdx.x,
-// blockIdx.x + gridDim.x, ...  Only partitions that exist are ever visited, so
-// no workgroup is spent on the empty tail of an upper-bound grid.  Each item
-// issues the next one's query rows and first K/V tiles before its epilogue.
+// Compact persistent split-KV.  Every workgroup first builds, in LDS, two
+// prefixes over sequences: of their full partitions (H_kv * floor(L / P)
+// items) and of their short last partitions (H_kv items when P does not
+// divide L).  Items are numbered full partitions first (sequence, kv head,
+// partition), then the short ones (sequence, kv head), so the last round of
+// the schedule holds the smallest items.  Workgroup w takes items w,
+// w + active, w + 2 active, ...  With `total` items over a grid of gridDim.x
+// workgroups the busiest ones take k = ceil(total / gridDim.x) items; when
+// ceil(total / k) workgroups (all holding k or k - 1 items) still fill at
+// least seven eighths of the grid, only those take part, so that no
+// workgroup runs a last item alone while the rest of the GPU idles;
+// otherwise all gridDim.x do.  Only partitions that exist are visited.  Each
+// item issues the next one's query rows and first K/V tiles before its
+// epilogue.
 constexpr int kCompactMaxSeqs = 1024;
 
 template <int D, int G, int NW, int DEPTH, bool FP8, bool XP>
@@ -704,64 +712,105 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     constexpr int T = NW * 64;
     constexpr int PER = (kCompactMaxSeqs + T - 1) / T;
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
-    __shared__ int pref[kCompactMaxSeqs + 1];
+    __shared__ int fpref[kCompactMaxSeqs + 1];  // full-partition items before sequence s
+    __shared__ int tpref[kCompactMaxSeqs + 1];  // short-partition items before sequence s
     __shared__ int lens[kCompactMaxSeqs];
-    __shared__ int wtot[NW];
+    __shared__ int wtot[2][NW];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nseq = prm.num_seqs, P = prm.partition_size, hkv = prm.num_kv_heads;
 
-    int cnt[PER];
-    int local = 0;
+    int cf[PER], ct[PER];
+    int lf = 0, lt = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int i = tid * PER + k;
-        int c = 0;
+        int f = 0, t = 0;
         if (i < nseq) {
             const int L = prm.seq_lens[i];
-            c = L > 0 ? hkv * ((L + P - 1) / P) : 0;
+            if (L > 0) {
+                f = hkv * (L / P);
+                t = (L % P) ? hkv : 0;
+            }
             lens[i] = L;
         }
-        cnt[k] = c;
-        local += c;
+        cf[k] = f;
+        ct[k] = t;
+        lf += f;
+        lt += t;
     }
-    int incl = local;
+    int inf = lf, intl = lt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
+        const int yf = __shfl_up(inf, d), yt = __shfl_up(intl, d);
+        if (lane >= d) {
+            inf += yf;
+            intl += yt;
+        }
     }
-    if (lane == 63) wtot[wave] = incl;
+    if (lane == 63) {
+        wtot[0][wave] = inf;
+        wtot[1][wave] = intl;
+    }
     __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wave; ++w) run += wtot[w];
+    int runf = inf - lf, runt = intl - lt;
+    for (int w = 0; w < wave; ++w) {
+        runf += wtot[0][w];
+        runt += wtot[1][w];
+    }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int i = tid * PER + k;
-        run += cnt[k];
-        if (i < nseq) pref[i + 1] = run;
+        runf += cf[k];
+        runt += ct[k];
+        if (i < nseq) {
+            fpref[i + 1] = runf;
+            tpref[i + 1] = runt;
+        }
     }
-    if (tid == 0) pref[0] = 0;
+    if (tid == 0) {
+        fpref[0] = 0;
+        tpref[0] = 0;
+    }
     __syncthreads();
 
-    const int total = __builtin_amdgcn_readfirstlane(pref[nseq]);  // uniform loop bound
-    // item -> its description: (sequence, kv head, partition) is found as the
-    // largest s with pref[s] <= item, then the rest within the sequence
-    auto locate = [&](int item) {
+    const int nfull = __builtin_amdgcn_readfirstlane(fpref[nseq]);
+    const int total = nfull + __builtin_amdgcn_readfirstlane(tpref[nseq]);  // uniform loop bound
+    const int per_wg = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    // (measured on MI355X: worth it when it idles at most an eighth of the
+    // grid; below that, the lost memory parallelism costs more than the
+    // last round's imbalance)
+    const int balanced = per_wg > 0 ? (total + per_wg - 1) / per_wg : 0;
+    const int active = 8 * balanced >= 7 * (int)gridDim.x ? balanced : min(total, (int)gridDim.x);
+    // item -> (sequence, kv head, partition): the largest s with pref[s] <=
+    // item (a sequence that has items of that kind), then the rest within it
+    auto search = [&](const int *pref, int item) {
         int lo = 0, hi = nseq;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (pref[mid] <= item) lo = mid; else hi = mid;
         }
-        const int seq = __builtin_amdgcn_readfirstlane(lo);
-        const int np = (pref[seq + 1] - pref[seq]) / hkv;
-        const int rr = item - pref[seq];
-        const int kvh = __builtin_amdgcn_readfirstlane(rr / np);
-        const int part = __builtin_amdgcn_readfirstlane(rr % np);
-        return make_item<NW>(prm, seq, kvh, part, lens[seq], wave, lane);
+        return __builtin_amdgcn_readfirstlane(lo);
+    };
+    auto locate = [&](int item) {
+        int seq, kvh, part;
+        if (item < nfull) {
+            seq = search(fpref, item);
+            const int nf = (fpref[seq + 1] - fpref[seq]) / hkv;
+            const int rr = item - fpref[seq];
+            kvh = rr / nf;
+            part = rr % nf;
+        } else {
+            const int r = item - nfull;
+            seq = search(tpref, r);
+            kvh = r - tpref[seq];
+            part = lens[seq] / P;
+        }
+        return make_item<NW>(prm, seq, __builtin_amdgcn_readfirstlane(kvh), __builtin_amdgcn_readfirstlane(part),
+                             lens[seq], wave, lane);
     };
     int item = blockIdx.x;
-    if (item >= total) return;
+    if (item >= active) return;
     DecodeItem it = locate(item);
     // Settle the first item's block-id load here: the wait the compiler would
     // otherwise place at the top of the item loop (where it would also drain
@@ -771,7 +820,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     bool primed = false;
     for (;;) {
         // the next item's block ids are fetched while this one streams
-        const int next = item + gridDim.x;
+        const int next = item + active;
         const bool has_next = next < total;
         const DecodeItem nx = has_next ? locate(next) : it;
         decode_item<D, G, NW, DEPTH, true, FP8, XP>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
