@@ -158,6 +158,12 @@ struct DecodeItem {
     int t_end, b_begin, my_nb, ids;
 };
 
+// Token-granular cache, persistent launch: the 16 slot ids of the lane's tile
+// of an item (tokens past the end: slot 0), held in registers until staged.
+struct TokIds {
+    u32x4 v[4];
+};
+
 template <int NW, bool TOK = false>
 __device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq, int kvh, int part,
                                                 int L, int wave, int lane) {
@@ -176,6 +182,33 @@ __device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq
     const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + it.b_begin + wave;
     it.ids = (!TOK && lane < min(64, it.my_nb)) ? bt_row[NW * lane] : 0;  // (token ids: staged in LDS)
     return it;
+}
+
+// Token-granular cache: the slot ids of the lane's tile of item `it`
+// (sequence it.seq's indices start at kv_indptr[it.seq]).
+template <int NW>
+__device__ __forceinline__ TokIds load_item_ids(const DecodeParams &prm, const DecodeItem &it, int wave,
+                                                int lane) {
+    int v[kBlock];
+    const bool mine = lane < min(64, it.my_nb);
+    const int tok0 = (it.b_begin + wave + NW * lane) * kBlock;
+    const int32_t *idx = prm.block_tables + (mine ? prm.kv_indptr[it.seq] : 0);
+#pragma unroll
+    for (int k = 0; k < kBlock; ++k) v[k] = (mine && tok0 + k < it.t_end) ? idx[tok0 + k] : 0;
+    TokIds t;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        t.v[k] = u32x4{(uint32_t)v[4 * k], (uint32_t)v[4 * k + 1], (uint32_t)v[4 * k + 2], (uint32_t)v[4 * k + 3]};
+    return t;
+}
+
+// ... and into the wave's LDS id region (tile `lane` at 16 * lane).
+__device__ __forceinline__ void stage_item_ids(const DecodeItem &it, const TokIds &t, int *ids, int lane) {
+    if (lane < min(64, it.my_nb)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(ids + lane * kBlock + 4 * k) = t.v[k];
+    }
+    wave_lds_sync();
 }
 
 // Workgroup barrier for LDS traffic only: unlike __syncthreads it does not
@@ -213,10 +246,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
                                             u32x4 (&qb)[D / 32],
                                             u32x4 (&kbuf)[DEPTH + 1][KvWords<D, FP8>::N],
                                             u32x4 (&vbuf)[DEPTH + 1][KvWords<D, FP8>::N], float *lds,
-                                            int *tok_lds = nullptr) {
+                                            int *tok_lds = nullptr, int *tok_nx_lds = nullptr,
+                                            const TokIds *nx_tk = nullptr) {
     using S = DecodeShape<D, G, NW>;
     static_assert(!(FP8 && XP), "the x-packed layout holds bf16");
-    static_assert(!(TOK && (FP8 || XP || ONE_CHUNK)), "the token-granular cache: bf16, grid launch");
+    static_assert(!(TOK && (FP8 || XP)), "the token-granular cache holds bf16 rows");
     constexpr int NJ = S::NJ, NDT = S::NDT, VROW = S::VROW;
     constexpr int NW16 = KvWords<D, FP8>::N;      // words per ring slot
     // V tile loads: a token row is LPT lanes of 16 bytes (8 bf16 or 16 E4M3
@@ -294,19 +328,24 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     // Token-granular cache: per-lane row gathers.  The slot ids of the wave's
     // chunk sit in LDS (stage_tok_ids); tiles past the chunk read slot 0 (they
     // are prefetched but never computed), so every load stays in bounds.
+    // (persistent launch: the caller staged this item's ids, and this item
+    // stages the next one's into `nx_ids` before issuing its first tiles)
     int *my_ids = TOK ? tok_lds + wave * kTokIdsPerWave : nullptr;
-    auto load_tile_tok = [&](int j, int n, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
-        const bool cur = j < n;
+    int *nx_ids = (TOK && ONE_CHUNK) ? tok_nx_lds + wave * kTokIdsPerWave : nullptr;
+    auto load_rows = [&](const int *ids, int hk, bool cur, int j, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
         const long row_stride = (long)prm.num_kv_heads * D;  // elements per slot
-        const long sk = cur ? my_ids[j * kBlock + col] : 0;
-        const uint16_t *kp = prm.k_cache + sk * row_stride + kvh * D + (grp * 8);
+        const long sk = cur ? ids[j * kBlock + col] : 0;
+        const uint16_t *kp = prm.k_cache + sk * row_stride + hk * D + (grp * 8);
 #pragma unroll
         for (int j2 = 0; j2 < NK; ++j2) kr[j2] = load_u32x4(kp + j2 * 32);
 #pragma unroll
         for (int j2 = 0; j2 < NV; ++j2) {
-            const long sv = cur ? my_ids[j * kBlock + vrow + j2 * TPI] : 0;
-            vr[j2] = load_u32x4(prm.v_cache + sv * row_stride + kvh * D + vcol * 8);
+            const long sv = cur ? ids[j * kBlock + vrow + j2 * TPI] : 0;
+            vr[j2] = load_u32x4(prm.v_cache + sv * row_stride + hk * D + vcol * 8);
         }
+    };
+    auto load_tile_tok = [&](int j, int n, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
+        load_rows(my_ids, kvh, j < n, j, kr, vr);
     };
     auto load_tile = [&](int ids, int j, int n, bool last, u32x4 (&kr)[NW16], u32x4 (&vr)[NW16]) {
         if constexpr (TOK) {
@@ -456,7 +495,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
             wave_lds_sync();
         }
     };
-    if (TOK) stage_tok_ids(0, min(64, my_nb));
+    if (TOK && !ONE_CHUNK) stage_tok_ids(0, min(64, my_nb));
     if (!primed) {
         load_q(seq, kvh);
 #pragma unroll
@@ -492,8 +531,15 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         }
     }
     if (has_next) {
-        // a wave that streamed nothing has not issued the next item's tiles yet
-        if (my_nb == 0) {
+        if constexpr (TOK) {
+            // the next item's slot ids (loaded when this item began) into
+            // its LDS region, then its first tiles
+            stage_item_ids(nx, *nx_tk, nx_ids, lane);
+            const int nn = min(64, nx_nb);
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) load_rows(nx_ids, nx_kvh, d < nn, d, kbuf[d], vbuf[d]);
+        } else if (my_nb == 0) {
+            // a wave that streamed nothing has not issued the next item's tiles yet
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) load_tile(0, d, 0, true, kbuf[d], vbuf[d]);
         }
@@ -706,12 +752,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
 // epilogue.
 constexpr int kCompactMaxSeqs = 1024;
 
-template <int D, int G, int NW, int DEPTH, bool FP8, bool XP>
+template <int D, int G, int NW, int DEPTH, bool FP8, bool XP, bool TOK = false>
 __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodeParams prm) {
     using S = DecodeShape<D, G, NW>;
     constexpr int T = NW * 64;
     constexpr int PER = (kCompactMaxSeqs + T - 1) / T;
     __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    // token-granular cache: two id regions per wave (this item, the next)
+    __shared__ __attribute__((aligned(16))) int tok_ids[TOK ? 2 * NW * kTokIdsPerWave : 1];
     __shared__ int fpref[kCompactMaxSeqs + 1];  // full-partition items before sequence s
     __shared__ int tpref[kCompactMaxSeqs + 1];  // short-partition items before sequence s
     __shared__ int lens[kCompactMaxSeqs];
@@ -727,7 +775,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
         const int i = tid * PER + k;
         int f = 0, t = 0;
         if (i < nseq) {
-            const int L = prm.seq_lens[i];
+            const int L = TOK ? prm.kv_indptr[i + 1] - prm.kv_indptr[i] : prm.seq_lens[i];
             if (L > 0) {
                 f = hkv * (L / P);
                 t = (L % P) ? hkv : 0;
@@ -806,8 +854,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
             kvh = r - tpref[seq];
             part = lens[seq] / P;
         }
-        return make_item<NW>(prm, seq, __builtin_amdgcn_readfirstlane(kvh), __builtin_amdgcn_readfirstlane(part),
-                             lens[seq], wave, lane);
+        return make_item<NW, TOK>(prm, seq, __builtin_amdgcn_readfirstlane(kvh),
+                                  __builtin_amdgcn_readfirstlane(part), lens[seq], wave, lane);
     };
     int item = blockIdx.x;
     if (item >= active) return;
@@ -816,18 +864,27 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
     // otherwise place at the top of the item loop (where it would also drain
     // the prefetched loads of every later item) becomes a no-op.
     __builtin_amdgcn_s_waitcnt(0);
+    int buf = 0;  // token-granular cache: the id region of the current item
+    if constexpr (TOK) stage_item_ids(it, load_item_ids<NW>(prm, it, wave, lane), tok_ids + wave * kTokIdsPerWave, lane);
     u32x4 qb[D / 32], kbuf[DEPTH + 1][KvWords<D, FP8>::N], vbuf[DEPTH + 1][KvWords<D, FP8>::N];
     bool primed = false;
     for (;;) {
-        // the next item's block ids are fetched while this one streams
+        // the next item's block (or slot) ids are fetched while this one streams
         const int next = item + active;
         const bool has_next = next < total;
         const DecodeItem nx = has_next ? locate(next) : it;
-        decode_item<D, G, NW, DEPTH, true, FP8, XP>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
+        TokIds nx_tk;
+        if constexpr (TOK) {
+            if (has_next) nx_tk = load_item_ids<NW>(prm, nx, wave, lane);
+        }
+        decode_item<D, G, NW, DEPTH, true, FP8, XP, TOK>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds,
+                                                         tok_ids + buf * NW * kTokIdsPerWave,
+                                                         tok_ids + (buf ^ 1) * NW * kTokIdsPerWave, &nx_tk);
         if (!has_next) break;
         item = next;
         it = nx;
         primed = true;
+        buf ^= 1;
     }
 }
 
@@ -1088,20 +1145,20 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
                      a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
                      a.tmp_out, a.counters, a.k_scales, a.v_scales, a.kv_indptr};
     dim3 block(kDecodeWaves * 64);
-    if (!TOK && a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock &&
+    if (a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock &&
         a.num_seqs <= kCompactMaxSeqs) {
         static int per_cu = 0;  // resident workgroups per CU for this instantiation
         if (per_cu == 0) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP>, block.x, 0) != hipSuccess || n <= 0)
+                    &n, paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP, TOK>, block.x, 0) != hipSuccess || n <= 0)
                 n = 1;
             per_cu = PA_DECODE_PERSIST_PER_CU > 0 ? PA_DECODE_PERSIST_PER_CU : n;
         }
         const long upper = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
         const long cap = (long)cu_count() * per_cu;
         dim3 grid((unsigned)(upper < cap ? upper : cap));
-        hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP>), grid, block, 0,
+        hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP, TOK>), grid, block, 0,
                            a.stream, prm);
     } else {
         dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);

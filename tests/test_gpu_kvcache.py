@@ -347,6 +347,10 @@ TOK_CASES = [
     ("G=6 D=256", [1, 100, 1030], 12, 2, 256, (0, 256)),
     ("G=1 D=64, a zero length", [3, 0, 64, 700], 2, 2, 64, (0, 64)),
     ("G=8 D=128, many chunks", [5000, 40], 16, 2, 128, (0, 1024)),
+    # enough items that persistent workgroups take several each (the next
+    # item's slot ids and first rows are fetched before an item's epilogue)
+    ("G=4 D=128, several items per workgroup",
+     [int(x) for x in np.random.default_rng(77).integers(200, 900, size=48)], 8, 2, 128, (32, 64)),
 ]
 
 
