@@ -482,18 +482,37 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
         fpref[p] = frun;
         frun += fl[k];
     }
-    // bitonic sort of the keys, ascending (longest remainder first, then pair)
-    for (int k = 2; k <= kPfMaxPairs; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const int i = 2 * tid - (tid & (j - 1));
-            const int l = i + j;
-            const int a = rorder[i], b = rorder[l];
-            if ((a > b) == ((i & k) == 0)) {
-                rorder[i] = b;
-                rorder[l] = a;
-            }
-            __syncthreads();
+    // bitonic sort of the keys, ascending (longest remainder first, then
+    // pair), over the first power of two >= NP entries (the rest are unused
+    // pairs, keyed last already).  Up to 128 entries one wave sorts alone: its
+    // LDS accesses execute in program order, so no barrier is needed between
+    // stages; more entries take the workgroup, a barrier per stage.
+    int n2 = 2;
+    while (n2 < NP) n2 <<= 1;
+    auto cmp_exchange = [&](int t, int k, int j) {
+        const int i = 2 * t - (t & (j - 1));
+        const int l = i + j;
+        const int a = rorder[i], b = rorder[l];
+        if ((a > b) == ((i & k) == 0)) {
+            rorder[i] = b;
+            rorder[l] = a;
         }
+    };
+    if (n2 <= 128) {
+        if (wave == 0) {
+            for (int k = 2; k <= n2; k <<= 1)
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    if (lane < n2 / 2) cmp_exchange(lane, k, j);
+                    __builtin_amdgcn_wave_barrier();
+                }
+        }
+        __syncthreads();
+    } else {
+        for (int k = 2; k <= n2; k <<= 1)
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                if (tid < n2 / 2) cmp_exchange(tid, k, j);
+                __syncthreads();
+            }
     }
     int nrem_local = 0;
 #pragma unroll
