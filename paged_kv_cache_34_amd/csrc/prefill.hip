@@ -66,10 +66,6 @@ __device__ __forceinline__ float max_xor32_pf(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float max_xor16_pf(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 __device__ __forceinline__ float sum_xor32_pf(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -667,118 +663,6 @@ __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfPa
     }
 }
 
-// Merge of the split-KV partial records for few chunks per row: one wave per
-// (new row, query head), rows indexed over the whole batch.  The wave's lanes
-// form R = 256 / D rows of D / 4 lanes (4 dims per lane) that take the row's
-// chunks round-robin, 4 at a time with every load issued before any is used,
-// each keeping a running maximum; the rows are then folded with lane swaps
-// (symmetric, so every lane of a fold holds the same value).  When every
-// chunk slot fits in the first round, the records are loaded before the
-// row's chunk count is known (records past its chunks are discarded by
-// selection, never used in arithmetic), in the same memory round trip as the
-// sequences' offsets and lengths; a row's sequence is then found in LDS.
-// Rows whose keys all lie in the first chunk were written by the chunk
-// kernel and are left alone.
-constexpr int kPfMergeUnroll = 4;
-constexpr int kPfMergeMaxRounds = 8;  // chunks per row beyond R * 4 * this use paged_prefill_merge_kernel
-
-template <int D>
-__global__ __launch_bounds__(256) void paged_prefill_merge_wave_kernel(PfParams prm) {
-    constexpr int LPR = D / 4;   // lanes per row
-    constexpr int R = 64 / LPR;  // rows per wave
-    constexpr int U = kPfMergeUnroll;
-    __shared__ int s_cu[kPfMaxSeqs + 1], s_len[kPfMaxSeqs];
-    const int lane = threadIdx.x & 63;
-    const int hq = prm.num_q_heads, S = prm.num_seqs;
-    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // batch row * H_q + head
-    const bool live = pair < (long)prm.total_q * hq;
-    const int r = lane / LPR, d0 = 4 * (lane % LPR);
-    const float *mr = prm.ws_m + pair * prm.max_splits;
-    const float *lr = prm.ws_l + pair * prm.max_splits;
-    const float *orr = prm.ws_o + pair * prm.max_splits * (long)D + d0;
-    const bool speculate = prm.max_splits <= R * U;
-    float mv[U], lv[U];
-    f32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int p = r + u * R;
-        const bool in = live && speculate && p < prm.max_splits;
-        mv[u] = in ? mr[p] : -INFINITY;
-        lv[u] = in ? lr[p] : 0.f;
-        v[u] = in ? *reinterpret_cast<const f32x4 *>(orr + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int i = threadIdx.x; i <= S; i += 256) s_cu[i] = prm.cu_seqlens[i];
-    for (int i = threadIdx.x; i < S; i += 256) s_len[i] = prm.seq_lens[i];
-    __syncthreads();
-    if (!live) return;
-    const int row = (int)(pair / hq);
-    int lo = 0, hi = S;  // the sequence holding `row`: the largest s with cu[s] <= row
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_cu[mid] <= row) lo = mid; else hi = mid;
-    }
-    const int n = s_cu[lo + 1] - s_cu[lo];
-    const int visible = s_len[lo] - n + (row - s_cu[lo]) + 1;
-    const int ns = (visible + prm.chunk - 1) / prm.chunk;
-    if (ns <= 1) return;  // written directly by the chunk kernel
-    if (!speculate) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = r + u * R;
-            const bool in = p < ns;
-            mv[u] = in ? mr[p] : -INFINITY;
-            lv[u] = in ? lr[p] : 0.f;
-            v[u] = in ? *reinterpret_cast<const f32x4 *>(orr + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    float m = -INFINITY, wsum = 0.f;  // (log2 units, as the records)
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = r;; p0 += R * U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (p0 + u * R >= ns) continue;
-            if (mv[u] > m) {  // rescale what was accumulated to the new max
-                const float f = fast_exp2(m - mv[u]);
-                acc *= f;
-                wsum *= f;
-                m = mv[u];
-            }
-            const float w = fast_exp2(mv[u] - m) * lv[u];
-            acc[0] = fmaf(w, v[u][0], acc[0]);
-            acc[1] = fmaf(w, v[u][1], acc[1]);
-            acc[2] = fmaf(w, v[u][2], acc[2]);
-            acc[3] = fmaf(w, v[u][3], acc[3]);
-            wsum += w;
-        }
-        const int q0 = p0 + R * U;
-        if (__all(q0 >= ns)) break;  // wave-uniform exit; rows past ns load nothing below
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = q0 + u * R;
-            const bool ok = p < ns;
-            mv[u] = ok ? mr[p] : -INFINITY;
-            lv[u] = ok ? lr[p] : 0.f;
-            v[u] = ok ? *reinterpret_cast<const f32x4 *>(orr + (long)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    // fold the rows: rescale each to the common max, then sum
-    auto fold = [&](auto max_x, auto sum_x) {
-        const float M = max_x(m);
-        const float f = wsum > 0.f ? fast_exp2(m - M) : 0.f;
-        wsum = sum_x(f * wsum);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = sum_x(f * acc[k]);
-        m = M;
-    };
-    if constexpr (R >= 4) fold([](float x) { return max_xor16_pf(x); }, [](float x) { return sum_xor16(x); });
-    if constexpr (R >= 2) fold([](float x) { return max_xor32_pf(x); }, [](float x) { return sum_xor32(x); });
-    if (r == 0) {
-        const float inv = 1.f / wsum;
-        *reinterpret_cast<u32x2 *>(prm.out + pair * D + d0) =
-            u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-    }
-}
-
 namespace {
 int pf_cu_count() {
     static int cached[64] = {0};
@@ -812,15 +696,8 @@ hipError_t launch_prefill_dg(const PrefillArgs &a) {
                            a.stream, prm);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        constexpr int rows_per_wave = 256 / D;
-        if (a.max_splits <= rows_per_wave * kPfMergeUnroll * kPfMergeMaxRounds) {
-            const long pairs = (long)a.total_q * a.num_q_heads;
-            hipLaunchKernelGGL((paged_prefill_merge_wave_kernel<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
-                               a.stream, prm);
-        } else {
-            hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.max_q_len, a.num_seqs), dim3(kMergeThreads),
-                               0, a.stream, prm);
-        }
+        hipLaunchKernelGGL((paged_prefill_merge_kernel<D>), dim3(a.max_q_len, a.num_seqs), dim3(kMergeThreads), 0,
+                           a.stream, prm);
         return hipGetLastError();
     }
     dim3 grid((a.max_q_len + R - 1) / R, a.num_kv_heads, a.num_seqs);
