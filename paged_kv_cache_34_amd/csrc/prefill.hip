@@ -132,9 +132,13 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, grp = lane >> 5;
+    // slots are row-major (slot = row * G + head), so the waves of a short
+    // last query tile that hold only padding rows are the high ones, one per
+    // SIMD (waves w and w + 4 share a SIMD), and skip their math
     const int slot = wave * 32 + col;
-    const int hq = slot / R, rq = slot % R;          // head within group, row within tile
-    const bool q_ok = hq < G && rq < rows;
+    const int hq = slot % G, rq = slot / G;          // head within group, row within tile
+    const bool q_ok = rq < rows;
+    const bool wave_live = __builtin_amdgcn_readfirstlane((wave * 32) / G) < rows;
     const int limit = c + r0 + rq;                   // last visible key of this slot
 
     // query slot as the B operand of S^T: 8 consecutive d per lane per k-step
@@ -308,7 +312,7 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
     // the other LDS buffer; slot u is refilled with tile tt + DEPTH + 1.
     auto step = [&](int tt, auto uc) {
         constexpr int u = decltype(uc)::value;
-        compute(tt, tt & 1);
+        if (wave_live) compute(tt, tt & 1);
         store_lds((tt + 1) & 1, kreg[(u + 1) % (DEPTH + 1)], vreg[(u + 1) % (DEPTH + 1)]);
         load_regs(tt + DEPTH + 1, kreg[u], vreg[u]);
         __syncthreads();
