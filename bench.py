@@ -522,8 +522,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the decode would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the decode would shard by sequence or by kv head, one GPU per share). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

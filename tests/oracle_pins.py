@@ -676,7 +676,7 @@ def run_all(path: str) -> List[str]:
             fn(orc)
         except AssertionError as e:
             failed.append(f"{name}: {str(e)[:120]}")
-        except Exception as e:  # a crash inside a pin also rejects the build
+        except Exception as e:  # a crash inside a pin also rejects the oracle library under test
             failed.append(f"{name}: {type(e).__name__} {str(e)[:120]}")
     return failed
 
