@@ -390,8 +390,12 @@ int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, in
     const long long pairs = ceil_div(total_q, rows) + num_seqs;
     if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs || num_q_heads > pa::kPfMaxHeads) return 0;
     const long long lmax = (long long)max_blocks_per_seq * block_size;
-    // about eight chunks per CU if every pair had the longest context
-    const long long target = 8LL * device_cu_count();
+    // about three chunks per CU if every pair had the longest context
+    // (measured on MI355X over 512..8192-token chunks on a ragged batch of
+    // 16 sequences: fewer, longer chunks win until the last ones unbalance
+    // the grid -- each chunk costs a start-up of dependent loads and its
+    // rows' partial records)
+    const long long target = 3LL * device_cu_count();
     long long chunk = ceil_div(pairs * num_kv_heads * lmax, target);
     chunk = ceil_div(chunk, kChunkQuantum) * kChunkQuantum;
     if (chunk < kMinChunk) chunk = kMinChunk;
