@@ -391,8 +391,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PfParams p
 // Chunk order: all full chunks (pair, kv head, chunk), then the remainder
 // chunks by decreasing length (pair order among equals; a bitonic sort of the
 // pairs keeps it deterministic, so every workgroup sees the same list).
-// Workgroups take chunk indices from counters[0]; the last workgroup to
-// finish resets both counters to zero for the next launch.
+// Workgroup w takes chunk w first, then chunk indices gridDim.x +
+// counters[0]++; the last workgroup to finish resets both counters to zero
+// for the next launch.
 template <int D, int G>
 __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfParams prm) {
     constexpr int R = kPfSlots / G;
@@ -521,11 +522,15 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
     block_scan(nrem_local, NR);
     const int total = F + NR * hkv;
 
-    // 3. take chunks
-    for (;;) {
-        if (tid == 0) bcast[0] = atomicAdd(prm.counters, 1);
-        __syncthreads();
-        const int it = __builtin_amdgcn_readfirstlane(bcast[0]);
+    // 3. take chunks: the first is blockIdx.x, the later ones come from the
+    // device counter (offset by the grid)
+    for (bool first = true;; first = false) {
+        int it = blockIdx.x;
+        if (!first) {
+            if (tid == 0) bcast[0] = (int)gridDim.x + atomicAdd(prm.counters, 1);
+            __syncthreads();
+            it = __builtin_amdgcn_readfirstlane(bcast[0]);
+        }
         if (it >= total) break;
         int p, kvh, split;
         if (it < F) {
