@@ -303,6 +303,7 @@ def run_decode(args, pa):
     kern_gbps = kv_bytes / (ms_kernel * 1e-3) / 1e9
     traffic = counter_traffic("decode_fp8" if fp8 else "decode_xpacked" if xp else "decode",
                               DECODE_SOURCE, args.workload)
+    ceiling = None if args.no_read_ceiling else read_ceiling(pa, kv_bytes, copies)
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -341,7 +342,7 @@ def run_decode(args, pa):
             "bound": "hbm",
             "kernel": ("paged_decode_compact_kernel (fused merge)" if fused else "paged_decode_compact_kernel")
                       + (" <FP8>" if fp8 else "") + (" <x-packed>" if xp else "")
-                      + (" <token-granular, grid launch>" if tok else ""),
+                      + (" <token-granular>" if tok else ""),
             "achieved": kern_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -351,7 +352,53 @@ def run_decode(args, pa):
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    if ceiling is not None:
+        ceiling["kernel_frac_of_same_bytes_read"] = kern_gbps / ceiling["same_bytes_rotated_gbps"]
+        ceiling["kernel_frac_of_large_read"] = kern_gbps / ceiling["large_buffer_gbps"]
+        result["read_ceiling"] = ceiling
     return result, cases[0]
+
+
+def read_ceiling(pa, nbytes: int, copies: int):
+    """Measured HBM read ceiling from the library's read-stream probe: the best
+    rate over grids of 16..256 workgroups per CU, on one large buffer (steady
+    streaming) and on `copies` rotated buffers of `nbytes` each (the decode's
+    own bytes per launch, read cold)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+
+    def rate(bufs, nwg, reps):
+        partial = torch.empty(nwg, dtype=torch.int32, device="cuda")
+        for i in range(3):
+            pa.paged_attn_read_probe(bufs[i % len(bufs)], partial, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            pa.paged_attn_read_probe(bufs[i % len(bufs)], partial, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return bufs[0].numel() * bufs[0].element_size() / (ms * 1e-3) / 1e9, ms, nwg
+
+    grids = [m * cus for m in (16, 32, 64, 128, 256)]
+    big = [torch.empty(1 << 30, dtype=torch.int32, device="cuda")]       # 4 GiB
+    large_gbps, _, large_nwg = max(rate(big, g, 8) for g in grids)
+    del big
+    n16 = (nbytes + 15) // 16 * 4
+    same = [torch.empty(n16, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    same_gbps, same_ms, same_nwg = max(rate(same, g, 30) for g in grids)
+    del same
+    torch.cuda.empty_cache()
+    log(f"read ceiling: {large_gbps:.0f} GB/s over 4 GiB ({large_nwg} workgroups), {same_gbps:.0f} GB/s "
+        f"over {copies} rotated buffers of {nbytes / 1e6:.1f} MB ({same_ms * 1e3:.1f} us each, "
+        f"{same_nwg} workgroups)")
+    return {"probe": "paged_attn_read_probe (16-byte nontemporal loads, XOR-folded), best of "
+                     "16..256 workgroups per CU",
+            "large_buffer_bytes": 1 << 32, "large_buffer_gbps": large_gbps, "large_buffer_workgroups": large_nwg,
+            "same_bytes": nbytes, "same_bytes_rotated_copies": copies,
+            "same_bytes_rotated_gbps": same_gbps, "same_bytes_ms": same_ms, "same_bytes_workgroups": same_nwg}
 
 
 def run_prefill(args, pa):
@@ -516,6 +563,8 @@ def main():
                     help="ragged_prefill: split-KV entry point (default) or the single-pass one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the read-stream probe that measures the HBM read ceiling (decode workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (the reference kernel for HBM counter scaling)")
     args = ap.parse_args()

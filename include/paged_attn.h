@@ -332,6 +332,27 @@ int paged_attn_choose_partition_size(int num_seqs, int num_kv_heads, int max_seq
 int paged_attn_prefill_tile_map(const int32_t *cu_seqlens_host, int num_seqs, int tile_rows,
                                 int32_t *tile_to_batch, int32_t *tile_to_index, int capacity);
 
+/*
+ * HBM read-stream probe: a measurement helper beside the attention path, not
+ * a step of it.  The AstrAI "CUDA Kernels" page ("Known Optimization
+ * Targets") rates its decode by achieved against theoretical bandwidth; this
+ * call measures the achievable read rate on the device at hand, so a decode
+ * can also be rated against that.  It reads each of the `bytes` bytes at
+ * `buf` once (16-byte nontemporal loads, grid-stride over num_workgroups
+ * workgroups of 256 threads) and writes to partial[w] the XOR of the 32-bit
+ * words that workgroup w read: the XOR over all num_workgroups entries equals
+ * the XOR of every 32-bit word of the buffer.
+ *   buf             device memory, 16-byte aligned, read only.
+ *   bytes           a positive multiple of 16.
+ *   partial         device memory, uint32 [num_workgroups], written only.
+ *   num_workgroups  >= 1 (the grid; a few times 256 CUs x 8 fills the chip).
+ * Errors: PA_ERR_NULL_POINTER, PA_ERR_BAD_SHAPE (bytes, num_workgroups),
+ * PA_ERR_ALIGNMENT (buf), PA_ERR_LAUNCH.  Enqueued on `stream`; the caller
+ * owns both buffers.
+ */
+int paged_attn_read_probe(const void *buf, long long bytes, uint32_t *partial, int num_workgroups,
+                          void *stream);
+
 /* Human-readable name of a status code. */
 const char *paged_attn_status_string(int status);
 

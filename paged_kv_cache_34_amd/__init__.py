@@ -71,6 +71,7 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_num_partitions.argtypes = [_i, _i, _i]
         lib.paged_attn_choose_partition_size.argtypes = [_i, _i, _i, ctypes.c_long]
         lib.paged_attn_prefill_tile_map.argtypes = [_vp, _i, _i, _vp, _vp, _i]
+        lib.paged_attn_read_probe.argtypes = [_vp, ctypes.c_longlong, _vp, _i, _vp]
         lib.paged_attn_status_string.argtypes = [_i]
         lib.paged_attn_status_string.restype = ctypes.c_char_p
         for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
@@ -80,7 +81,7 @@ def library() -> ctypes.CDLL:
                    "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
                    "paged_attn_prefill_chunk_size",
                    "paged_attn_num_partitions", "paged_attn_choose_partition_size",
-                   "paged_attn_prefill_tile_map"):
+                   "paged_attn_prefill_tile_map", "paged_attn_read_probe"):
             getattr(lib, fn).restype = _i
         _lib = lib
     return _lib
@@ -446,6 +447,20 @@ def paged_attn_prefill_tile_map(cu_seqlens_host, tile_rows: int) -> Tuple[list, 
     ti = (ctypes.c_int32 * max(count, 1))()
     library().paged_attn_prefill_tile_map(cu, n, int(tile_rows), tb, ti, count)
     return list(tb[:count]), list(ti[:count])
+
+
+def paged_attn_read_probe(buf, partial, stream=None) -> None:
+    """HBM read-stream probe over every byte of the contiguous device tensor
+    `buf` (its size a multiple of 16 bytes); one workgroup per element of the
+    int32 tensor `partial`, which receives each workgroup's XOR of the 32-bit
+    words it read."""
+    import torch
+    _want(partial, torch.int32, "partial")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    _check("paged_attn_read_probe",
+           library().paged_attn_read_probe(_ptr(buf), nbytes, _ptr(partial), partial.numel(), _stream(stream)))
 
 
 def paged_attn_status_string(status: int) -> str:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libpaged_attn.so")
-SOURCES = ["api.hip", "decode.hip", "decode_fp8.hip", "decode_xpacked.hip", "decode_tokens.hip", "prefill.hip", "kvcache.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_fp8.hip", "decode_xpacked.hip", "decode_tokens.hip", "prefill.hip", "kvcache.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

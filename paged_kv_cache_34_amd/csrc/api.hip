@@ -264,6 +264,16 @@ int paged_attn_kv_append_fp8(const void *k_new, const void *v_new, const int32_t
                          max_blocks_per_seq, k_cache, v_cache, k_scales, v_scales, true, stream);
 }
 
+int paged_attn_read_probe(const void *buf, long long bytes, uint32_t *partial, int num_workgroups,
+                          void *stream) {
+    if (!buf || !partial) return PA_ERR_NULL_POINTER;
+    if (bytes <= 0 || bytes % 16 != 0 || num_workgroups <= 0) return PA_ERR_BAD_SHAPE;
+    if (!aligned16(buf)) return PA_ERR_ALIGNMENT;
+    const hipError_t e = pa::launch_read_probe(buf, bytes, partial, num_workgroups,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,

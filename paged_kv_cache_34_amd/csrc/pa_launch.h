@@ -85,5 +85,7 @@ hipError_t launch_prefill(const PrefillArgs &a);
 hipError_t launch_kv_append(const AppendArgs &a);
 hipError_t launch_kv_append_fp8(const AppendArgs &a);
 hipError_t launch_kv_append_xpacked(const AppendArgs &a);
+hipError_t launch_read_probe(const void *buf, long long bytes, uint32_t *partial, int num_workgroups,
+                             hipStream_t stream);
 
 }  // namespace pa

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_prefill_tile_map", "paged_attn_status_string", "paged_attn_decode_fp8",
         "paged_attn_kv_append", "paged_attn_kv_append_fp8", "paged_attn_decode_xpacked",
         "paged_attn_kv_append_xpacked", "paged_attn_decode_tokens",
-        "paged_attn_decode_reduce_indptr"} | (
+        "paged_attn_decode_reduce_indptr", "paged_attn_read_probe"} | (
         set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
     for name in names:
         assert hasattr(lib, name), name
@@ -381,3 +381,16 @@ def test_reduce_indptr_validation(lib):
     st = lib.paged_attn_decode_reduce_indptr(FAKE, FAKE, FAKE, FAKE, 2, 4, 80, 16, 7, FAKE, None)
     assert st == pa.PA_ERR_UNSUPPORTED
     assert lib.paged_attn_decode_reduce_indptr(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, 16, 7, FAKE, None) == pa.PA_OK
+
+
+@pytest.mark.parametrize("buf,nbytes,part,nwg,status", [
+    (NULL, 1024, FAKE, 8, pa.PA_ERR_NULL_POINTER),
+    (FAKE, 1024, NULL, 8, pa.PA_ERR_NULL_POINTER),
+    (FAKE, 0, FAKE, 8, pa.PA_ERR_BAD_SHAPE),
+    (FAKE, -16, FAKE, 8, pa.PA_ERR_BAD_SHAPE),
+    (FAKE, 1000, FAKE, 8, pa.PA_ERR_BAD_SHAPE),    # not a multiple of 16 bytes
+    (FAKE, 1024, FAKE, 0, pa.PA_ERR_BAD_SHAPE),
+    (FAKE + 8, 1024, FAKE, 8, pa.PA_ERR_ALIGNMENT),
+])
+def test_read_probe_validation(lib, buf, nbytes, part, nwg, status):
+    assert lib.paged_attn_read_probe(buf, nbytes, part, nwg, None) == status

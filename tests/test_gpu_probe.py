@@ -1,0 +1,43 @@
+"""GPU check of the HBM read-stream probe through the C ABI: the XOR of the
+per-workgroup words must equal the XOR of every 32-bit word of the buffer
+(integer work, compared exactly), for ragged sizes and several grids.
+Needs an MI355X."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_34_amd as pa
+from tests.gpu_util import announce, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def host_xor(words: np.ndarray) -> int:
+    return int(np.bitwise_xor.reduce(words.view(np.uint32)))
+
+
+@pytest.mark.parametrize("n_words,nwg", [
+    (4, 1),                  # one 16-byte word, one workgroup
+    (4 * 1001, 3),           # fewer words than lanes in the grid
+    (4 * 1_000_003, 37),     # ragged against the unrolled stride
+    (4 * 1_000_003, 2048),
+    (1 << 24, 8192),         # 64 MiB, the unrolled loop and no tail
+])
+def test_read_probe_xor(n_words, nwg):
+    t = torch()
+    announce(f"read probe: {n_words * 4} bytes, {nwg} workgroups")
+    rng = np.random.default_rng(n_words + nwg)
+    host = rng.integers(0, 2 ** 32, size=n_words, dtype=np.uint64).astype(np.uint32)
+    buf = t.from_numpy(host.view(np.int32)).cuda()
+    partial = t.full((nwg,), -1, dtype=t.int32, device="cuda")
+    pa.paged_attn_read_probe(buf, partial)
+    t.cuda.synchronize()
+    got = host_xor(partial.cpu().numpy())
+    assert got == host_xor(host)
+
+
+def test_read_probe_status_through_binding():
+    t = torch()
+    buf = t.zeros(5, dtype=t.int32, device="cuda")   # 20 bytes: not a multiple of 16
+    partial = t.zeros(4, dtype=t.int32, device="cuda")
+    with pytest.raises(pa.PagedAttnError):
+        pa.paged_attn_read_probe(buf, partial)
