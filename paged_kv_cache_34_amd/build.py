@@ -32,8 +32,14 @@ def hipcc() -> str:
 
 
 def _flags():
+    # -amdgpu-mfma-vgpr-form: MFMA accumulators in arch VGPRs.  With the
+    # default AGPR form the decode tile loop copied all its PV accumulators
+    # AGPR -> VGPR on every iteration (for the rarely taken softmax rescale),
+    # about a third of its vector ALU work, and the FP8 decode kernels needed
+    # more registers (D=256: one wave per SIMD instead of two).
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
