@@ -99,11 +99,17 @@ int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
  * BI-V100 design page, section 2 "Level 3": "a separate reduction kernel (or
  * the last partition block)" -- this is the second option).  Same inputs and
  * partial buffers as paged_attn_decode with partition_size > 0, which here
- * are workspace; writes the bf16 `out` for every sequence in one launch.
- * Each workgroup that writes a partial record increments the arrival counter
- * of its (sequence, kv head); the workgroup completing the set merges the
- * ceil(L / P) records in partition order (deterministic) and resets the
- * counter.  Sequences with a single partition write `out` directly.
+ * are workspace (their contents are not partition partials); writes the bf16
+ * `out` for every sequence in one launch, zero rows for zero-length
+ * sequences.  Schedule: with up to 1024 sequences and max_num_partitions >= 2
+ * (and ceil(max_blocks_per_seq / (max_num_partitions - 1)) <= 256), the
+ * tiles of all (sequence, kv head) pairs are split evenly across the
+ * workgroups (stream-K): each workgroup's share of a pair leaves one record,
+ * at most max_num_partitions per pair; otherwise one record per partition of
+ * partition_size tokens.  Each workgroup that writes a record increments the
+ * arrival counter of its (sequence, kv head); the workgroup completing the
+ * set merges the records in token order (deterministic) and resets the
+ * counter.  A pair whose tokens form a single record writes `out` directly.
  *   counters  int32 [num_seqs * num_kv_heads], device memory, all zero on
  *             entry (e.g. cleared once after allocation); every completed call
  *             leaves them zero.  Calls that overlap in time must not share a

@@ -66,6 +66,9 @@ struct DecodeParams {
     uint16_t *out;
     float *max_logits, *exp_sums, *tmp_out;
     int *counters;  // fused merge: one arrival counter per (sequence, kv head); null = no merge
+    // fused merge, stream-K schedule: the smallest unit (in 16-token tiles)
+    // that keeps every (sequence, kv head) within max_num_partitions records
+    int sk_min_tiles;
     // FP8 cache: dequant multipliers [num_blocks, H_kv, 16] (k_cache / v_cache
     // then hold E4M3 codes [num_blocks, H_kv, 16, D]); null for a bf16 cache
     const float *k_scales, *v_scales;
@@ -156,6 +159,7 @@ __device__ __forceinline__ float load_partial(float *p) {
 struct DecodeItem {
     int seq, kvh, part, L;
     int t_end, b_begin, my_nb, ids;
+    int nrec;  // records of the item's (sequence, kv head): its partitions, or its stream-K segments
 };
 
 // Token-granular cache, persistent launch: the 16 slot ids of the lane's tile
@@ -176,11 +180,33 @@ __device__ __forceinline__ DecodeItem make_item(const DecodeParams &prm, int seq
     it.part = part;
     it.L = L;
     it.t_end = P ? min(L, t_begin + P) : L;
+    it.nrec = P ? (L + P - 1) / P : 1;
     it.b_begin = t_begin / kBlock;
     const int nb = (it.t_end + kBlock - 1) / kBlock - it.b_begin;
     it.my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
     const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + it.b_begin + wave;
     it.ids = (!TOK && lane < min(64, it.my_nb)) ? bt_row[NW * lane] : 0;  // (token ids: staged in LDS)
+    return it;
+}
+
+// A stream-K segment: tiles [tile0, tile1) of kv head `kvh` of sequence
+// `seq`, record `ord` of the pair's `nrec` (bf16 block cache only).
+template <int NW>
+__device__ __forceinline__ DecodeItem make_segment(const DecodeParams &prm, int seq, int kvh, int ord, int nrec,
+                                                   int L, int tile0, int tile1, int wave, int lane) {
+    DecodeItem it;
+    L = __builtin_amdgcn_readfirstlane(L);
+    it.seq = seq;
+    it.kvh = kvh;
+    it.part = ord;
+    it.nrec = nrec;
+    it.L = L;
+    it.t_end = min(L, tile1 * kBlock);
+    it.b_begin = tile0;
+    const int nb = tile1 - tile0;
+    it.my_nb = nb > wave ? (nb - wave + NW - 1) / NW : 0;
+    const int32_t *bt_row = prm.block_tables + (long)seq * prm.max_blocks_per_seq + it.b_begin + wave;
+    it.ids = lane < min(64, it.my_nb) ? bt_row[NW * lane] : 0;
     return it;
 }
 
@@ -577,7 +603,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     // (single pass, or the fused mode with one partition); otherwise its
     // partial record.
     const long row0 = (long)seq * num_q_heads + h0;
-    const int nparts = partition_size ? (L + partition_size - 1) / partition_size : 1;
+    const int nparts = __builtin_amdgcn_readfirstlane(it.nrec);
     const bool direct = partition_size == 0 || (fused && nparts == 1);
     for (int e = tid; e < G * D; e += NW * 64) {
         const int h = e / D, d = e % D;
@@ -752,6 +778,18 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_grid_kernel(DecodeParams
 // epilogue.
 constexpr int kCompactMaxSeqs = 1024;
 
+// Zero output rows for the zero-length sequences (lengths staged in LDS):
+// sequence s by workgroup s mod grid.
+template <int D>
+__device__ __forceinline__ void write_empty_rows(const DecodeParams &prm, const int *lens) {
+    const int T = blockDim.x, row = prm.num_q_heads * D;
+    for (int s = blockIdx.x; s < prm.num_seqs; s += gridDim.x) {
+        if (lens[s] > 0) continue;
+        uint16_t *o = prm.out + (long)s * row;
+        for (int e = threadIdx.x; e < row; e += T) o[e] = 0;
+    }
+}
+
 template <int D, int G, int NW, int DEPTH, bool FP8, bool XP, bool TOK = false>
 __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodeParams prm) {
     using S = DecodeShape<D, G, NW>;
@@ -857,6 +895,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
         return make_item<NW, TOK>(prm, seq, __builtin_amdgcn_readfirstlane(kvh),
                                   __builtin_amdgcn_readfirstlane(part), lens[seq], wave, lane);
     };
+    // the fused merge writes `out` itself: zero-length sequences, which have
+    // no items, get zero rows here (a workgroup per sequence, round-robin)
+    if (prm.counters) write_empty_rows<D>(prm, lens);
     int item = blockIdx.x;
     if (item >= active) return;
     DecodeItem it = locate(item);
@@ -885,6 +926,111 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_compact_kernel(DecodePar
         it = nx;
         primed = true;
         buf ^= 1;
+    }
+}
+
+// Fused merge, stream-K schedule (bf16 block cache): the tiles of all
+// (sequence, kv head) pairs laid end to end, pair-major in (sequence, kv head)
+// order, are cut into equal units of at most NW * 64 tiles (one block-id
+// chunk per wave) and workgroup w takes k consecutive units, so every
+// workgroup streams the same number of tiles however the lengths are spread.
+// A unit's part of one pair is a segment, processed as one item; its record
+// goes to slot (unit - first unit of the pair) of the pair's records, and the
+// workgroup completing a pair's records merges them in slot order (the fused
+// epilogue of decode_item).  `sk_min_tiles` (host) bounds the records per
+// pair by max_num_partitions: a pair of nt <= max_blocks_per_seq tiles meets
+// at most ceil(nt / unit) + 1 units.
+template <int D, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void paged_decode_streamk_kernel(DecodeParams prm) {
+    using S = DecodeShape<D, G, NW>;
+    constexpr int T = NW * 64;
+    constexpr int PER = (kCompactMaxSeqs + T - 1) / T;
+    constexpr long kUnitMax = NW * 64;
+    __shared__ __attribute__((aligned(16))) float lds[S::MAIN_FLOATS + S::STAT_FLOATS];
+    __shared__ int tp[kCompactMaxSeqs + 1];  // tiles of one kv head of the sequences before s
+    __shared__ int lens[kCompactMaxSeqs];
+    __shared__ int wtot[NW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nseq = prm.num_seqs, hkv = prm.num_kv_heads;
+
+    int ct[PER];
+    int lt = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid * PER + k;
+        int nt = 0;
+        if (i < nseq) {
+            const int L = prm.seq_lens[i];
+            nt = L > 0 ? (L + kBlock - 1) / kBlock : 0;
+            lens[i] = L;
+        }
+        ct[k] = nt;
+        lt += nt;
+    }
+    int incl = lt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int run = incl - lt;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid * PER + k;
+        run += ct[k];
+        if (i < nseq) tp[i + 1] = run;
+    }
+    if (tid == 0) tp[0] = 0;
+    __syncthreads();
+    write_empty_rows<D>(prm, lens);
+
+    const long total = (long)__builtin_amdgcn_readfirstlane(tp[nseq]) * hkv;
+    const long grid = gridDim.x;
+    const long per = (total + grid - 1) / grid;
+    const long k = (per + kUnitMax - 1) / kUnitMax;  // units per workgroup
+    long unit = k > 0 ? (total + grid * k - 1) / (grid * k) : 1;
+    if (unit < prm.sk_min_tiles) unit = prm.sk_min_tiles;
+    const long x0 = (long)blockIdx.x * k * unit;
+    const long xe = min(total, x0 + k * unit);
+    if (x0 >= xe) return;
+
+    // the segment starting at tile x of the global order, and where it ends
+    auto segment = [&](long x, long &end) {
+        int lo = 0, hi = nseq;  // the largest s with tp[s] * hkv <= x (a sequence with tiles, as x < total)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((long)tp[mid] * hkv <= x) lo = mid; else hi = mid;
+        }
+        const int seq = __builtin_amdgcn_readfirstlane(lo);
+        const int nt = tp[seq + 1] - tp[seq];
+        const long base = (long)tp[seq] * hkv;
+        const int kvh = __builtin_amdgcn_readfirstlane((int)((x - base) / nt));
+        const long ps = base + (long)kvh * nt, pe = ps + nt;
+        const long u = x / unit;
+        end = min(pe, (u + 1) * unit);
+        const int ord = __builtin_amdgcn_readfirstlane((int)(u - ps / unit));
+        const int nrec = __builtin_amdgcn_readfirstlane((int)((pe - 1) / unit - ps / unit + 1));
+        return make_segment<NW>(prm, seq, kvh, ord, nrec, lens[seq], (int)(x - ps), (int)(end - ps), wave, lane);
+    };
+    long x_end;
+    DecodeItem it = segment(x0, x_end);
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 qb[D / 32], kbuf[DEPTH + 1][KvWords<D, false>::N], vbuf[DEPTH + 1][KvWords<D, false>::N];
+    bool primed = false;
+    for (;;) {
+        const bool has_next = x_end < xe;
+        long nx_end = x_end;
+        DecodeItem nx = it;
+        if (has_next) nx = segment(x_end, nx_end);
+        decode_item<D, G, NW, DEPTH, true, false, false>(prm, it, nx, has_next, primed, qb, kbuf, vbuf, lds);
+        if (!has_next) break;
+        it = nx;
+        x_end = nx_end;
+        primed = true;
     }
 }
 
@@ -1147,8 +1293,33 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
     DecodeParams prm{a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
                      a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.scale_log2,
                      a.partition_size, a.max_num_partitions, a.out, a.max_logits, a.exp_sums,
-                     a.tmp_out, a.counters, a.k_scales, a.v_scales, a.kv_indptr};
+                     a.tmp_out, a.counters, 0, a.k_scales, a.v_scales, a.kv_indptr};
     dim3 block(kDecodeWaves * 64);
+    // Fused merge over a bf16 block cache: the stream-K schedule, when its
+    // smallest unit that keeps each pair within max_num_partitions records
+    // (ceil(max_blocks_per_seq / (max_num_partitions - 1)) tiles) fits one
+    // block-id chunk per wave.
+    if constexpr (!FP8 && !XP && !TOK) {
+        const long unit_max = kDecodeWaves * 64;
+        if (a.counters && a.partition_size > 0 && a.num_seqs <= kCompactMaxSeqs && a.max_num_partitions >= 2) {
+            const long sk_min = ((long)a.max_blocks_per_seq + a.max_num_partitions - 2) / (a.max_num_partitions - 1);
+            if (sk_min <= unit_max) {
+                prm.sk_min_tiles = (int)sk_min;
+                static int per_cu = 0;
+                if (per_cu == 0) {
+                    int n = 0;
+                    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &n, paged_decode_streamk_kernel<D, G, kDecodeWaves, DEPTH>, block.x, 0) != hipSuccess || n <= 0)
+                        n = 1;
+                    per_cu = n;
+                }
+                dim3 grid((unsigned)(cu_count() * per_cu));
+                hipLaunchKernelGGL((paged_decode_streamk_kernel<D, G, kDecodeWaves, DEPTH>), grid, block, 0,
+                                   a.stream, prm);
+                return hipGetLastError();
+            }
+        }
+    }
     if (a.partition_size > 0 && a.partition_size <= kDecodeWaves * 64 * kBlock &&
         a.num_seqs <= kCompactMaxSeqs) {
         static int per_cu = 0;  // resident workgroups per CU for this instantiation

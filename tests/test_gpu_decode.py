@@ -280,3 +280,19 @@ def test_fused_merge(orc, name, P):
     assert int(ws.counters.abs().sum().item()) == 0, "arrival counters must be left at zero"
     out2, _ = run_fused(dev, P, ws)  # the same workspace again
     assert np.array_equal(bf16_bits_host(out), bf16_bits_host(out2))
+
+
+def test_fused_merge_zero_length_sequence(orc):
+    """The fused path writes `out` itself, zero rows included (sequences of
+    length 0 have no work items)."""
+    case = workloads.build_case("fused_zero", 308, [5, 0, 70, 0, 600], 4, 2, 64)
+    dev = Dev(case)
+    ref = orc.decode_case(case)
+    announce("fused merge with zero-length sequences")
+    for P in (32, 512):
+        out, ws = run_fused(dev, P)
+        got = bf16_host_f64(out)
+        assert np.all(got[[1, 3]] == 0.0)
+        assert_out_close(got[[0, 2, 4]], ref[[0, 2, 4]], f"fused zero-length neighbours P={P}")
+        assert int(ws.counters.abs().sum().item()) == 0
+
