@@ -290,6 +290,25 @@ def run_decode(args, pa):
     k1.record(stream)
     torch.cuda.synchronize()
     ms_kernel = k0.elapsed_time(k1) / args.steps
+    # timed region 3 (bf16 block cache, separate merge timed above): the same
+    # steps through the fused entry point, reported beside the main line
+    ms_fused = None
+    if P and not (fused or fp8 or xp or tok):
+        def fused_step(i):
+            d = devs[i % copies]
+            pa.paged_attn_decode_fused(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P, out,
+                                       ws.max_logits, ws.exp_sums, ws.tmp_out, ws.counters,
+                                       stream=stream)
+        for i in range(args.warmup):
+            fused_step(i)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for i in range(args.steps):
+            fused_step(i)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ms_fused = f0.elapsed_time(f1) / args.steps
     # leave the output of a full step behind (the partials above are not merged)
     step(0)
     torch.cuda.synchronize()
@@ -352,6 +371,12 @@ def run_decode(args, pa):
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    if ms_fused is not None:
+        result["fused_merge"] = {
+            "entry_point": "paged_attn_decode_fused (stream-K schedule, merge in the last workgroup)",
+            "ms_per_step": ms_fused, "value": tokens / (ms_fused * 1e-3), "unit": "KV tokens/s",
+            "hbm_gbps": kv_bytes / (ms_fused * 1e-3) / 1e9,
+            "frac_of_peak": kv_bytes / (ms_fused * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     if ceiling is not None:
         ceiling["kernel_frac_of_same_bytes_read"] = kern_gbps / ceiling["same_bytes_rotated_gbps"]
         ceiling["kernel_frac_of_large_read"] = kern_gbps / ceiling["large_buffer_gbps"]
