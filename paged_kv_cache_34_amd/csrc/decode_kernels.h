@@ -293,7 +293,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     // (the item fields are wave-uniform; say so, since values carried around
     // the persistent loop may sit in vector registers)
     const int seq = __builtin_amdgcn_readfirstlane(it.seq), kvh = __builtin_amdgcn_readfirstlane(it.kvh);
-    const int part = __builtin_amdgcn_readfirstlane(it.part), L = __builtin_amdgcn_readfirstlane(it.L);
+    const int part = __builtin_amdgcn_readfirstlane(it.part);
     const int t_end = __builtin_amdgcn_readfirstlane(it.t_end);
     const int b_begin = __builtin_amdgcn_readfirstlane(it.b_begin);
     const int my_nb = __builtin_amdgcn_readfirstlane(it.my_nb);

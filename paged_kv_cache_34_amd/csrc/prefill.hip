@@ -404,7 +404,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
     __shared__ PfLds<D> lds;
     __shared__ int pr_seq[kPfMaxPairs], pr_qt[kPfMaxPairs], pr_kv[kPfMaxPairs];
     __shared__ int fpref[kPfMaxPairs], rorder[kPfMaxPairs];
-    __shared__ int bcnt[kPfMaxBuckets];
     __shared__ int wtot[kPfWaves], bcast[1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
