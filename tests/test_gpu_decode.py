@@ -296,3 +296,22 @@ def test_fused_merge_zero_length_sequence(orc):
         assert_out_close(got[[0, 2, 4]], ref[[0, 2, 4]], f"fused zero-length neighbours P={P}")
         assert int(ws.counters.abs().sum().item()) == 0
 
+
+@pytest.mark.parametrize("name,P,extra", [("llama3", 512, 3), ("edges", 256, 5)])
+def test_fused_merge_larger_record_workspace(orc, name, P, extra):
+    """A record workspace larger than the partition count lets the fused
+    schedule use smaller units (more records per sequence); the result and the
+    counters' reset must not depend on it."""
+    t = torch()
+    case = (workloads.llama3_8b_decode() if name == "llama3"
+            else workloads.build_case("fused_ws", 324, EDGE_LENS, 12, 2, 128))
+    dev = Dev(case)
+    ref = orc.decode_case(case)
+    npart = pa.paged_attn_num_partitions(case.max_blocks_per_seq, case.block_size, P)
+    ws = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart * extra, "cuda",
+                            num_kv_heads=case.num_kv_heads)
+    announce(f"fused merge {name} P={P} records x{extra}")
+    out, _ = run_fused(dev, P, ws)
+    assert_out_close(bf16_host_f64(out), ref, f"fused {name} P={P} records x{extra}")
+    assert int(ws.counters.abs().sum().item()) == 0
+
