@@ -309,6 +309,18 @@ def run_decode(args, pa):
         f1.record(stream)
         torch.cuda.synchronize()
         ms_fused = f0.elapsed_time(f1) / args.steps
+    # timed region 4: the step-time distribution (an event between steps) and
+    # the warm case (one pool copy reused, so part of it stays cached)
+    def per_step(fn, n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for i in range(n):
+            fn(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n)])
+    dist = per_step(step, max(args.steps, 100))
+    warm = per_step(lambda i: step(0), max(args.steps, 100))
     # leave the output of a full step behind (the partials above are not merged)
     step(0)
     torch.cuda.synchronize()
@@ -371,6 +383,12 @@ def run_decode(args, pa):
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    result["step_distribution"] = {
+        "per_step_events": int(dist.size), "median_ms": float(np.median(dist)),
+        "p10_ms": float(np.percentile(dist, 10)), "p90_ms": float(np.percentile(dist, 90)),
+        "warm_one_copy_median_ms": float(np.median(warm)),
+        "note": "an event between consecutive steps (timed separately from ms_per_step); warm = the "
+                "same pool copy every step, so part of it stays in the 256 MB Infinity Cache"}
     if ms_fused is not None:
         result["fused_merge"] = {
             "entry_point": "paged_attn_decode_fused (stream-K schedule, merge in the last workgroup)",
