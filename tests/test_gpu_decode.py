@@ -315,3 +315,20 @@ def test_fused_merge_larger_record_workspace(orc, name, P, extra):
     assert_out_close(bf16_host_f64(out), ref, f"fused {name} P={P} records x{extra}")
     assert int(ws.counters.abs().sum().item()) == 0
 
+
+@pytest.mark.parametrize("P", [2400, 1600, 512])
+def test_fused_merge_schedule_boundaries(orc, P):
+    """Sequences of up to 4,800 tokens (300 blocks): P = 2400 leaves two
+    record slots, too few for the stream-K schedule (it would need units of
+    300 tiles), so the partition schedule runs; P = 1600 (three slots, units
+    of at least 150 tiles) and P = 512 take the stream-K schedule."""
+    case = workloads.build_case("fused_bounds", 325, [4800, 1, 2399, 2401, 17, 4799, 3000], 8, 2, 128)
+    dev = Dev(case)
+    ref = orc.decode_case(case)
+    announce(f"fused merge schedule boundary P={P}")
+    out, ws = run_fused(dev, P)
+    assert_out_close(bf16_host_f64(out), ref, f"fused bounds P={P}")
+    assert int(ws.counters.abs().sum().item()) == 0
+    out2, _ = run_fused(dev, P, ws)
+    assert np.array_equal(bf16_bits_host(out), bf16_bits_host(out2))
+
