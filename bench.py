@@ -600,8 +600,9 @@ def main():
     ap.add_argument("--copies", type=int, default=None,
                     help="independent KV pool copies rotated across steps (default 3, or 2 for >1 GB pools)")
     ap.add_argument("--merge", default="separate", choices=["fused", "separate"],
-                    help="cross-partition merge: a separate kernel (default; faster on MI355X at "
-                         "these shapes) or fused into the partition kernel")
+                    help="cross-partition merge: a separate kernel (default: the reduce entry point "
+                         "of the C ABI) or fused into one launch (stream-K schedule; the default "
+                         "decode line also times it, as fused_merge)")
     ap.add_argument("--prefill-form", default="split", choices=["split", "single"],
                     help="ragged_prefill: split-KV entry point (default) or the single-pass one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
