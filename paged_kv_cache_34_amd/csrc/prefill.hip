@@ -579,6 +579,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
 constexpr int kMergeThreads = 256;
 constexpr int kMergeMaxHeads = kPfMaxHeads;  // query heads per row held in LDS
 constexpr int kMergeSplits = 32;             // chunks per row held in LDS per pass
+constexpr int kMergeSpecChunks = 4;          // fast path: at most this many chunks per row ...
+constexpr int kMergeSpecCols = 4;            // ... and 4-dim columns per thread
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfParams prm) {
@@ -603,6 +605,62 @@ __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfPa
             sl[h * SP + j] = prm.ws_l[r];
         }
     };
+    // Few chunks and at most kMergeSpecCols columns per thread: the chunk
+    // outputs are loaded together with the maxima and exp-sums (one round of
+    // loads instead of two); the arithmetic is that of the general path below.
+    if (ns <= kMergeSpecChunks && hq * (D / 4) <= kMergeSpecCols * T) {
+        f32x4 ov[kMergeSpecCols][kMergeSpecChunks];
+#pragma unroll
+        for (int k = 0; k < kMergeSpecCols; ++k) {
+            const int e = threadIdx.x + k * T;
+            if (e < hq * (D / 4)) {
+                const int h = e / (D / 4), d0 = (e % (D / 4)) * 4;
+                const float *o = prm.ws_o + (rec_row + (long)h * prm.max_splits) * D + d0;
+#pragma unroll
+                for (int j = 0; j < kMergeSpecChunks; ++j)
+                    if (j < ns) ov[k][j] = *reinterpret_cast<const f32x4 *>(o + (long)j * D);
+            }
+        }
+        stage(0, ns);
+        __syncthreads();
+        for (int h = threadIdx.x; h < hq; h += T) {
+            float M = -INFINITY, S = 0.f;
+            for (int j = 0; j < ns; ++j) {
+                const float mj = sm[h * SP + j];
+                if (mj > M) {
+                    S *= fast_exp2(M - mj);
+                    M = mj;
+                }
+                S += fast_exp2(mj - M) * sl[h * SP + j];
+            }
+            hmax[h] = M;
+            hsum[h] = S;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < hq * ns; e += T) {
+            const int h = e / ns, j = e - h * ns;
+            sm[h * SP + j] = fast_exp2(sm[h * SP + j] - hmax[h]) * sl[h * SP + j] / hsum[h];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMergeSpecCols; ++k) {
+            const int e = threadIdx.x + k * T;
+            if (e < hq * (D / 4)) {
+                const int h = e / (D / 4), d0 = (e % (D / 4)) * 4;
+                const float *w = sm + h * SP;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < kMergeSpecChunks; ++j)
+                    if (j < ns) acc += w[j] * ov[k][j];
+                uint16_t *orow = prm.out + ((long)row * hq + h) * D + d0;
+                u32x2 wv;
+                wv[0] = pack_bf16x2(acc[0], acc[1]);
+                wv[1] = pack_bf16x2(acc[2], acc[3]);
+                *reinterpret_cast<u32x2 *>(orow) = wv;
+            }
+        }
+        return;
+    }
     // per-head maximum and exp-sum over all chunks (online across passes)
     for (int j0 = 0; j0 < ns; j0 += SP) {
         const int nj = min(SP, ns - j0);
