@@ -484,9 +484,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
     }
     // bitonic sort of the keys, ascending (longest remainder first, then
     // pair), over the first power of two >= NP entries (the rest are unused
-    // pairs, keyed last already).  Up to 128 entries one wave sorts alone: its
-    // LDS accesses execute in program order, so no barrier is needed between
-    // stages; more entries take the workgroup, a barrier per stage.
+    // pairs, keyed last already).  Up to 64 entries one wave sorts them in
+    // registers; up to 128 one wave sorts them in LDS (its LDS accesses
+    // execute in program order, so no barrier is needed between stages); more
+    // entries take the workgroup, a barrier per stage.
     int n2 = 2;
     while (n2 < NP) n2 <<= 1;
     auto cmp_exchange = [&](int t, int k, int j) {
@@ -498,7 +499,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
             rorder[l] = a;
         }
     };
-    if (n2 <= 128) {
+    if (n2 <= 64) {
+        // one key per lane of wave 0; each stage exchanges with lane ^ j
+        // (the same network, in registers)
+        if (wave == 0) {
+            int key = rorder[lane];
+            for (int k = 2; k <= n2; k <<= 1)
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    const int other = __shfl_xor(key, j);
+                    const bool up = (lane & k) == 0, lower = (lane & j) == 0;
+                    key = (lower == up) ? min(key, other) : max(key, other);
+                }
+            if (lane < n2) rorder[lane] = key;
+        }
+        __syncthreads();
+    } else if (n2 <= 128) {
         if (wave == 0) {
             for (int k = 2; k <= n2; k <<= 1)
                 for (int j = k >> 1; j > 0; j >>= 1) {
