@@ -430,14 +430,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
         return run;
     };
 
-    // 1. pairs (sequence, query tile)
-    int nq[SPT];
+    // 1. pairs (sequence, query tile); the lengths are all loaded in one round
+    int nq[SPT], nn[SPT], sq[SPT];
     int local = 0;
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
         const int i = tid * SPT + k;
-        nq[k] = 0;
-        if (i < S) nq[k] = (prm.cu_seqlens[i + 1] - prm.cu_seqlens[i] + R - 1) / R;
+        nn[k] = 0;
+        sq[k] = 0;
+        if (i < S) {
+            nn[k] = prm.cu_seqlens[i + 1] - prm.cu_seqlens[i];
+            sq[k] = prm.seq_lens[i];
+        }
+        nq[k] = (nn[k] + R - 1) / R;
         local += nq[k];
     }
     int NP = 0;
@@ -447,8 +452,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
     for (int k = 0; k < SPT; ++k) {
         const int i = tid * SPT + k;
         if (i < S) {
-            const int n = prm.cu_seqlens[i + 1] - prm.cu_seqlens[i];
-            const int c = prm.seq_lens[i] - n;
+            const int n = nn[k];
+            const int c = sq[k] - n;
             for (int qt = 0; qt < nq[k] && run + qt < kPfMaxPairs; ++qt) {
                 pr_seq[run + qt] = i;
                 pr_qt[run + qt] = qt;
