@@ -96,8 +96,9 @@ int paged_attn_decode_reduce(const float *max_logits, const float *exp_sums,
 
 /*
  * Decode with the cross-partition merge fused into the partition kernel (the
- * BI-V100 design page, section 2 "Level 3": "a separate reduction kernel (or
- * the last partition block)" -- this is the second option).  Same inputs and
+ * BI-V100 design page, section 2 "Level 3", names two ways to merge: a
+ * separate kernel, or whichever partition block finishes last -- this is the
+ * second).  Same inputs and
  * partial buffers as paged_attn_decode with partition_size > 0, which here
  * are workspace (their contents are not partition partials); writes the bf16
  * `out` for every sequence in one launch, zero rows for zero-length

@@ -19,7 +19,8 @@ Definitions followed (details in the C source):
                  causal rule of the RL.cu page's prefill kernel, end-aligned.
   tile_map    -- AstrAI page, "Q Scheduling and KV Addressing" worked example.
   kv_append   -- the cache write before decode/prefill (AstrAI page, backend
-                 layer: it "owns KV cache writes and reads"); new rows are the
+                 layer, which is responsible for writing and reading the KV
+                 cache); new rows are the
                  last rows of each sequence, placed like the prefill rows.
   fp8         -- FP8 (OCP E4M3) KV cache with a per-position dequant scale (B200
                  page, "Stage D: FP8 Paged KV Gather" and "FP8 KV

@@ -53,8 +53,9 @@ int oracle_num_threads(void) {
 #endif
 }
 
-/* kv head serving query head h: consecutive query heads share one kv head
- * (RL.cu page, attention.cuh comment "kv_head = q_head * H_kv / H_q"). */
+/* kv head serving query head h: consecutive query heads share one kv head,
+ * the group of H_q / H_kv query heads mapping to it in order (RL.cu page,
+ * the head mapping of its attention header). */
 static int kv_head_of(int h, int Hq, int Hkv) {
 #if ORACLE_MUTANT == 2
     return h % Hkv;
@@ -451,7 +452,7 @@ int oracle_prefill(const uint16_t *q, const uint16_t *k_bits, const uint16_t *v_
 /* ---- KV cache writes ------------------------------------------------------ */
 
 /* KV append: the cache write that comes before decode and prefill (the AstrAI
- * page's backend layer "owns KV cache writes and reads"; the B200 page's paged
+ * page's backend layer is responsible for writing and reading the cache; the B200 page's paged
  * KV cache read/write).  Sequence s owns new rows [cu[s], cu[s+1]) of k_new /
  * v_new ([num_tokens, H_kv, D]); they are the last n = cu[s+1] - cu[s] of its
  * seq_lens[s] tokens, so row j goes to position c + j with c = L - n: block

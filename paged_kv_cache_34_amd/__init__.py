@@ -123,6 +123,34 @@ def _want(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t, shape, name, fn):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{fn}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_decode_buffers(fn, q, seq_lens, rows, out, partition_size, max_logits, exp_sums,
+                          tmp_out, max_num_partitions, counters=None, num_kv_heads=0):
+    """The library trusts its buffers to be as large as its size arguments
+    say; check every tensor against them before the call (a short buffer
+    would be read or written out of bounds on the device)."""
+    num_seqs, hq, d = q.shape
+    if seq_lens is not None and seq_lens.numel() != num_seqs:
+        raise ValueError(f"{fn}: seq_lens must have {num_seqs} entries, got {seq_lens.numel()}")
+    if rows is not None and rows.shape[0] != num_seqs:
+        raise ValueError(f"{fn}: block_tables must have {num_seqs} rows, got {rows.shape[0]}")
+    _shape(out, (num_seqs, hq, d), "out", fn)
+    if partition_size > 0:
+        if max_logits is None or exp_sums is None or tmp_out is None:
+            raise ValueError(f"{fn}: split-KV (partition_size > 0) needs max_logits, exp_sums and tmp_out")
+        np_ = int(max_num_partitions)
+        _shape(max_logits, (num_seqs, hq, np_), "max_logits", fn)
+        _shape(exp_sums, (num_seqs, hq, np_), "exp_sums", fn)
+        _shape(tmp_out, (num_seqs, hq, np_, d), "tmp_out", fn)
+    if counters is not None and counters.numel() < num_seqs * num_kv_heads:
+        raise ValueError(f"{fn}: counters must hold num_seqs * num_kv_heads = {num_seqs * num_kv_heads} "
+                         f"entries, got {counters.numel()}")
+
+
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
@@ -141,8 +169,11 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
         _want(t, torch.float32, name)
     num_seqs, hq, d = q.shape
     num_blocks, hkv, bs, _ = k_cache.shape
+    _shape(v_cache, k_cache.shape, "v_cache", "paged_attn_decode")
     if max_num_partitions is None:
         max_num_partitions = tmp_out.shape[2] if tmp_out is not None else 1
+    _check_decode_buffers("paged_attn_decode", q, seq_lens, block_tables, out, partition_size,
+                          max_logits, exp_sums, tmp_out, max_num_partitions)
     st = library().paged_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), num_seqs, hq,
         hkv, d, bs, num_blocks, block_tables.shape[1], float(scale), int(partition_size),
@@ -168,6 +199,11 @@ def paged_attn_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale: 
         _want(t, torch.float32, name)
     num_seqs, hq, d = q.shape
     num_blocks, hkv, bs, _ = k_cache.shape
+    _shape(v_cache, k_cache.shape, "v_cache", "paged_attn_decode_fused")
+    if tmp_out is None or tmp_out.dim() != 4:
+        raise ValueError("paged_attn_decode_fused: tmp_out must be [num_seqs, H_q, max_num_partitions, D]")
+    _check_decode_buffers("paged_attn_decode_fused", q, seq_lens, block_tables, out, partition_size,
+                          max_logits, exp_sums, tmp_out, tmp_out.shape[2], counters, hkv)
     st = library().paged_attn_decode_fused(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), num_seqs, hq,
         hkv, d, bs, num_blocks, block_tables.shape[1], float(scale), int(partition_size),
@@ -185,6 +221,11 @@ def paged_attn_decode_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_
     _want(seq_lens, torch.int32, "seq_lens")
     _want(out, torch.bfloat16, "out")
     s, hq, npart, d = tmp_out.shape
+    _shape(max_logits, (s, hq, npart), "max_logits", "paged_attn_decode_reduce")
+    _shape(exp_sums, (s, hq, npart), "exp_sums", "paged_attn_decode_reduce")
+    _shape(out, (s, hq, d), "out", "paged_attn_decode_reduce")
+    if seq_lens.numel() != s:
+        raise ValueError(f"paged_attn_decode_reduce: seq_lens must have {s} entries")
     st = library().paged_attn_decode_reduce(
         _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(seq_lens), s, hq, d,
         int(partition_size), npart, _ptr(out), _stream(stream))
@@ -210,8 +251,13 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, k_scales, v_scales, block_tables,
         _want(t, torch.float32, name)
     num_seqs, hq, d = q.shape
     num_blocks, hkv, bs, _ = k_cache.shape
+    _shape(v_cache, k_cache.shape, "v_cache", "paged_attn_decode_fp8")
+    _shape(k_scales, (num_blocks, hkv, bs), "k_scales", "paged_attn_decode_fp8")
+    _shape(v_scales, (num_blocks, hkv, bs), "v_scales", "paged_attn_decode_fp8")
     if max_num_partitions is None:
         max_num_partitions = tmp_out.shape[2] if tmp_out is not None else 1
+    _check_decode_buffers("paged_attn_decode_fp8", q, seq_lens, block_tables, out, partition_size,
+                          max_logits, exp_sums, tmp_out, max_num_partitions)
     st = library().paged_attn_decode_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
         _ptr(seq_lens), num_seqs, hq, hkv, d, bs, num_blocks, block_tables.shape[1], float(scale),
@@ -239,8 +285,12 @@ def paged_attn_decode_xpacked(q, k_cache, v_cache, block_tables, seq_lens, scale
         raise ValueError("k_cache must be [num_blocks, H_kv, D/8, bs, 8] and v_cache [num_blocks, H_kv, D, bs]")
     num_seqs, hq, d = q.shape
     num_blocks, hkv, _, bs = v_cache.shape
+    _shape(k_cache, (num_blocks, hkv, d // 8, bs, 8), "k_cache", "paged_attn_decode_xpacked")
+    _shape(v_cache, (num_blocks, hkv, d, bs), "v_cache", "paged_attn_decode_xpacked")
     if max_num_partitions is None:
         max_num_partitions = tmp_out.shape[2] if tmp_out is not None else 1
+    _check_decode_buffers("paged_attn_decode_xpacked", q, seq_lens, block_tables, out, partition_size,
+                          max_logits, exp_sums, tmp_out, max_num_partitions)
     st = library().paged_attn_decode_xpacked(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), num_seqs, hq,
         hkv, d, bs, num_blocks, block_tables.shape[1], float(scale), int(partition_size),
@@ -266,8 +316,13 @@ def paged_attn_decode_tokens(q, k_cache, v_cache, kv_indptr, kv_indices, max_kv_
         _want(t, torch.float32, name)
     num_seqs, hq, d = q.shape
     num_slots, hkv, _ = k_cache.shape
+    _shape(v_cache, k_cache.shape, "v_cache", "paged_attn_decode_tokens")
+    if kv_indptr.numel() != num_seqs + 1:
+        raise ValueError(f"paged_attn_decode_tokens: kv_indptr must have {num_seqs + 1} entries")
     if max_num_partitions is None:
         max_num_partitions = tmp_out.shape[2] if tmp_out is not None else 1
+    _check_decode_buffers("paged_attn_decode_tokens", q, None, None, out, partition_size,
+                          max_logits, exp_sums, tmp_out, max_num_partitions)
     st = library().paged_attn_decode_tokens(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr), _ptr(kv_indices), num_seqs, hq, hkv,
         d, num_slots, int(max_kv_len), float(scale), int(partition_size), _ptr(out), _ptr(max_logits),
@@ -284,6 +339,11 @@ def paged_attn_decode_reduce_indptr(max_logits, exp_sums, tmp_out, kv_indptr, pa
     _want(kv_indptr, torch.int32, "kv_indptr")
     _want(out, torch.bfloat16, "out")
     s, hq, npart, d = tmp_out.shape
+    _shape(max_logits, (s, hq, npart), "max_logits", "paged_attn_decode_reduce_indptr")
+    _shape(exp_sums, (s, hq, npart), "exp_sums", "paged_attn_decode_reduce_indptr")
+    _shape(out, (s, hq, d), "out", "paged_attn_decode_reduce_indptr")
+    if kv_indptr.numel() != s + 1:
+        raise ValueError(f"paged_attn_decode_reduce_indptr: kv_indptr must have {s + 1} entries")
     st = library().paged_attn_decode_reduce_indptr(
         _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(kv_indptr), s, hq, d,
         int(partition_size), npart, _ptr(out), _stream(stream))
@@ -474,10 +534,12 @@ class DecodeWorkspace:
     """fp32 partial buffers sized for (num_seqs, H_q, max_num_partitions, D), plus
     the zeroed arrival counters of the fused merge ([num_seqs * num_kv_heads])."""
 
-    def __init__(self, num_seqs, num_q_heads, head_dim, max_num_partitions, device,
-                 num_kv_heads: int = 0):
+    def __init__(self, num_seqs, num_q_heads, head_dim, max_num_partitions, device, *,
+                 num_kv_heads: int):
         import torch
         self.max_num_partitions = int(max_num_partitions)
+        if num_kv_heads <= 0 or num_q_heads % num_kv_heads:
+            raise ValueError("num_kv_heads must be a positive divisor of num_q_heads")
         self.counters = torch.zeros(max(1, num_seqs * num_kv_heads), dtype=torch.int32, device=device)
         self.max_logits = torch.empty((num_seqs, num_q_heads, max_num_partitions),
                                       dtype=torch.float32, device=device)

@@ -54,22 +54,10 @@ constexpr int kChunkTile = 64;       // key chunks are whole KV tiles (64 keys f
 constexpr int kChunkQuantum = 256;   // automatic chunk sizes are multiples of this
 constexpr int kMinChunk = 512;
 
-int device_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 }  // namespace
 
-extern "C" {
+// The entry points below take C linkage from their declarations in paged_attn.h.
 
 const char *paged_attn_status_string(int status) {
     switch (status) {
@@ -405,7 +393,7 @@ int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, in
     // 16 sequences: fewer, longer chunks win until the last ones unbalance
     // the grid -- each chunk costs a start-up of dependent loads and its
     // rows' partial records)
-    const long long target = 3LL * device_cu_count();
+    const long long target = 3LL * pa::device_cu_count();
     long long chunk = ceil_div(pairs * num_kv_heads * lmax, target);
     chunk = ceil_div(chunk, kChunkQuantum) * kChunkQuantum;
     if (chunk < kMinChunk) chunk = kMinChunk;
@@ -529,4 +517,3 @@ int paged_attn_decode_tokens(const void *q, const void *k_cache, const void *v_c
                          nullptr, stream, nullptr, nullptr, false, kv_indptr);
 }
 
-}  // extern "C"

@@ -1,6 +1,7 @@
 // KV cache writes for gfx950: the K/V rows of new tokens go to their cache
-// slots -- the write that comes before decode and prefill (the AstrAI page's
-// backend layer "owns KV cache writes and reads").  Either copied as bf16, or
+// slots -- the write that comes before decode and prefill (on the AstrAI
+// page the backend layer is responsible for cache writes as well as reads).
+// Either copied as bf16, or
 // quantized to FP8 (OCP E4M3) with one dequant scale per (position, kv head)
 // (the B200 page, "FP8 KV Quantize/Dequant" and the per-position dequant scale
 // of "Stage D: FP8 Paged KV Gather").

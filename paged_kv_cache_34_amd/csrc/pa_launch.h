@@ -5,7 +5,47 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace pa {
+
+// Per-device caches of launch facts (devices beyond kMaxDevices are queried
+// on every call).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (256 if the query fails).
+inline int device_cu_count() {
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const bool slot = dev >= 0 && dev < kMaxDevices;
+    if (slot) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (slot) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of KERN (at `threads` threads each, no dynamic LDS) resident per
+// compute unit of the current device, at least 1; cached per kernel and device.
+template <auto KERN>
+inline int resident_per_cu(int threads) {
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const bool slot = dev >= 0 && dev < kMaxDevices;
+    if (slot) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, threads, 0) != hipSuccess || n <= 0) n = 1;
+    if (slot) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 struct DecodeArgs {
     const uint16_t *q;

@@ -750,17 +750,6 @@ __global__ __launch_bounds__(kMergeThreads) void paged_prefill_merge_kernel(PfPa
 }
 
 namespace {
-int pf_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 template <int D, int G>
 hipError_t launch_prefill_dg(const PrefillArgs &a) {
@@ -770,15 +759,8 @@ hipError_t launch_prefill_dg(const PrefillArgs &a) {
                  a.scale_log2, a.out, a.chunk, a.max_splits, a.ws_m, a.ws_l, a.ws_o, a.counters};
     dim3 block(kPfWaves * 64);
     if (a.chunk > 0) {
-        static int per_cu = 0;  // resident workgroups per CU for this instantiation
-        if (per_cu == 0) {
-            int nb = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_prefill_split_kernel<D, G>,
-                                                             block.x, 0) != hipSuccess || nb <= 0)
-                nb = 1;
-            per_cu = nb;
-        }
-        hipLaunchKernelGGL((paged_prefill_split_kernel<D, G>), dim3(pf_cu_count() * per_cu), block, 0,
+        const int per_cu = resident_per_cu<paged_prefill_split_kernel<D, G>>(block.x);
+        hipLaunchKernelGGL((paged_prefill_split_kernel<D, G>), dim3(device_cu_count() * per_cu), block, 0,
                            a.stream, prm);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -30,8 +30,7 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_prefill_tile_map", "paged_attn_status_string", "paged_attn_decode_fp8",
         "paged_attn_kv_append", "paged_attn_kv_append_fp8", "paged_attn_decode_xpacked",
         "paged_attn_kv_append_xpacked", "paged_attn_decode_tokens",
-        "paged_attn_decode_reduce_indptr", "paged_attn_read_probe"} | (
-        set(n for n in names if n.startswith("paged_attn_decode_noalloc")))
+        "paged_attn_decode_reduce_indptr", "paged_attn_read_probe"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -394,3 +393,72 @@ def test_reduce_indptr_validation(lib):
 ])
 def test_read_probe_validation(lib, buf, nbytes, part, nwg, status):
     assert lib.paged_attn_read_probe(buf, nbytes, part, nwg, None) == status
+
+
+def test_decode_workspace_needs_kv_heads():
+    """The fused merge indexes its counters by (sequence, kv head): a workspace
+    must know the kv head count (no default that would size them for one)."""
+    with pytest.raises(TypeError):
+        pa.DecodeWorkspace(4, 8, 64, 2, "cpu")
+    with pytest.raises(ValueError):
+        pa.DecodeWorkspace(4, 8, 64, 2, "cpu", num_kv_heads=3)
+    ws = pa.DecodeWorkspace(4, 8, 64, 2, "cpu", num_kv_heads=2)
+    assert ws.counters.numel() == 8 and tuple(ws.tmp_out.shape) == (4, 8, 2, 64)
+
+
+def _decode_tensors(S=4, Hq=8, Hkv=2, D=64, NP=3, nb=20, mb=3):
+    import torch
+    return dict(q=torch.zeros((S, Hq, D), dtype=torch.bfloat16),
+                k=torch.zeros((nb, Hkv, 16, D), dtype=torch.bfloat16),
+                v=torch.zeros((nb, Hkv, 16, D), dtype=torch.bfloat16),
+                bt=torch.zeros((S, mb), dtype=torch.int32), sl=torch.ones(S, dtype=torch.int32),
+                out=torch.zeros((S, Hq, D), dtype=torch.bfloat16),
+                ml=torch.zeros((S, Hq, NP), dtype=torch.float32),
+                es=torch.zeros((S, Hq, NP), dtype=torch.float32),
+                to=torch.zeros((S, Hq, NP, D), dtype=torch.float32),
+                ctr=torch.zeros(S * Hkv, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("bad", ["counters", "max_logits", "exp_sums", "tmp_out", "out", "seq_lens",
+                                 "block_tables"])
+def test_fused_binding_checks_buffer_sizes(lib, bad):
+    """Every buffer of the fused entry point is checked against the sizes the
+    library will use, before the call (host tensors: nothing reaches a GPU)."""
+    import torch
+    t = _decode_tensors()
+    S, Hq, Hkv, D, NP = 4, 8, 2, 64, 3
+    if bad == "counters":
+        t["ctr"] = torch.zeros(S * Hkv - 1, dtype=torch.int32)
+    elif bad == "max_logits":
+        t["ml"] = torch.zeros((S, Hq, NP - 1), dtype=torch.float32)
+    elif bad == "exp_sums":
+        t["es"] = torch.zeros((S, Hq - 1, NP), dtype=torch.float32)
+    elif bad == "tmp_out":
+        t["to"] = torch.zeros((S, Hq, NP, D // 2), dtype=torch.float32)
+    elif bad == "out":
+        t["out"] = torch.zeros((S - 1, Hq, D), dtype=torch.bfloat16)
+    elif bad == "seq_lens":
+        t["sl"] = torch.ones(S - 1, dtype=torch.int32)
+    else:
+        t["bt"] = torch.zeros((S - 1, 3), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pa.paged_attn_decode_fused(t["q"], t["k"], t["v"], t["bt"], t["sl"], 0.125, 16, t["out"],
+                                   t["ml"], t["es"], t["to"], t["ctr"])
+
+
+@pytest.mark.parametrize("bad", ["max_logits", "tmp_out", "out"])
+def test_decode_binding_checks_partial_shapes(lib, bad):
+    import torch
+    t = _decode_tensors()
+    if bad == "max_logits":
+        t["ml"] = torch.zeros((4, 8, 2), dtype=torch.float32)
+    elif bad == "tmp_out":
+        t["to"] = torch.zeros((4, 8, 3, 32), dtype=torch.float32)
+    else:
+        t["out"] = torch.zeros((4, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.paged_attn_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], 0.125, 16, out=t["out"],
+                             max_logits=t["ml"], exp_sums=t["es"], tmp_out=t["to"])
+    with pytest.raises(ValueError):
+        pa.paged_attn_decode_reduce(t["ml"], t["es"], t["to"], t["sl"], 16, t["out"])
+

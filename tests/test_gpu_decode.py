@@ -31,7 +31,7 @@ def run_partials(dev, P):
     t = torch()
     c = dev.case
     npart = pa.paged_attn_num_partitions(c.max_blocks_per_seq, c.block_size, P)
-    ws = pa.DecodeWorkspace(c.num_seqs, c.num_q_heads, c.head_dim, npart, "cuda")
+    ws = pa.DecodeWorkspace(c.num_seqs, c.num_q_heads, c.head_dim, npart, "cuda", num_kv_heads=c.num_kv_heads)
     for buf in (ws.max_logits, ws.exp_sums, ws.tmp_out):
         buf.fill_(float("nan"))
     pa.paged_attn_decode(dev.q, dev.k, dev.v, dev.bt, dev.sl, float(c.scale), P,
@@ -332,3 +332,25 @@ def test_fused_merge_schedule_boundaries(orc, P):
     out2, _ = run_fused(dev, P, ws)
     assert np.array_equal(bf16_bits_host(out), bf16_bits_host(out2))
 
+
+
+def test_fused_merge_zero_length_many_sequences(orc):
+    """More than 1024 sequences send the fused entry point to the grid kernel
+    (one workgroup per partition slot); its zero-length sequences, which have
+    no partition to merge, must still get zero rows in an `out` that starts
+    as NaN."""
+    rng = np.random.default_rng(326)
+    lens = rng.integers(1, 300, size=1100)
+    lens[rng.choice(lens.size, 60, replace=False)] = 0
+    case = workloads.build_case("fused_many_zero", 326, lens, 8, 2, 64)
+    dev = Dev(case)
+    ref = orc.decode_case(case)
+    zero = np.flatnonzero(case.seq_lens == 0)
+    live = np.flatnonzero(case.seq_lens > 0)
+    for P in (64, 512):
+        announce(f"fused merge, 1100 sequences with 60 empty, P={P}")
+        out, ws = run_fused(dev, P)
+        got = bf16_host_f64(out)
+        assert np.all(got[zero] == 0.0), "zero-length rows must be zeros"
+        assert_out_close(got[live], ref[live], f"fused 1100 sequences P={P}")
+        assert int(ws.counters.abs().sum().item()) == 0

@@ -159,7 +159,7 @@ def test_decode_fp8_parity(orc, what, make, partitions):
             assert_out_close(bf16_host_f64(out), ref, f"fp8 {what} single pass")
             continue
         npart = pa.paged_attn_num_partitions(case.max_blocks_per_seq, 16, P)
-        ws = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
+        ws = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda", num_kv_heads=case.num_kv_heads)
         for b in (ws.max_logits, ws.exp_sums, ws.tmp_out):
             b.fill_(float("nan"))
         pa.paged_attn_decode_fp8(q, kc, vc, ksd, vsd, bt, sl, float(case.scale), P,
@@ -268,7 +268,7 @@ def run_decode_layouts(case, P):
             fn(q, kk, vv, bt, sl, float(case.scale), 0, out=out)
         else:
             npart = pa.paged_attn_num_partitions(case.max_blocks_per_seq, 16, P)
-            ws = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
+            ws = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda", num_kv_heads=case.num_kv_heads)
             for b in (ws.max_logits, ws.exp_sums, ws.tmp_out):
                 b.fill_(float("nan"))
             fn(q, kk, vv, bt, sl, float(case.scale), P, max_logits=ws.max_logits, exp_sums=ws.exp_sums,
@@ -371,7 +371,7 @@ def test_decode_tokens_parity(orc, what, lens, Hq, Hkv, D, partitions):
             assert_out_close(bf16_host_f64(out), ref, f"tokens {what} single pass")
             continue
         npart = pa.paged_attn_num_partitions((max_kv + 15) // 16, 16, P)
-        ws = pa.DecodeWorkspace(len(lens), Hq, D, npart, "cuda")
+        ws = pa.DecodeWorkspace(len(lens), Hq, D, npart, "cuda", num_kv_heads=Hkv)
         for b in (ws.max_logits, ws.exp_sums, ws.tmp_out):
             b.fill_(float("nan"))
         pa.paged_attn_decode_tokens(qd, kd, vd, ipd, ixd, max_kv, float(scale), P,
@@ -412,8 +412,8 @@ def test_decode_tokens_equals_block_cache_one_kv_head():
                                         float(case.scale), 0, out=b)
         else:
             npart = pa.paged_attn_num_partitions(case.max_blocks_per_seq, 16, P)
-            w1 = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
-            w2 = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda")
+            w1 = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda", num_kv_heads=case.num_kv_heads)
+            w2 = pa.DecodeWorkspace(case.num_seqs, case.num_q_heads, case.head_dim, npart, "cuda", num_kv_heads=case.num_kv_heads)
             pa.paged_attn_decode(dev.q, dev.k, dev.v, dev.bt, dev.sl, float(case.scale), P,
                                  max_logits=w1.max_logits, exp_sums=w1.exp_sums, tmp_out=w1.tmp_out,
                                  max_num_partitions=npart)
