@@ -48,7 +48,8 @@ enum paged_attn_status {
     PA_ERR_UNSUPPORTED = 3,   /* head_dim, block_size or GQA group outside the supported set */
     PA_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
     PA_ERR_ALIGNMENT = 5,     /* a bf16 / fp32 tensor pointer is not 16-byte aligned */
-    PA_ERR_BAD_VALUE = 6      /* scale is not a positive finite number */
+    PA_ERR_BAD_VALUE = 6,     /* scale is not a positive finite number */
+    PA_ERR_SCRATCH_LIMIT = 7  /* paged_attn_decode_fused_noalloc: the problem exceeds its fixed scratch */
 };
 
 /*
@@ -126,6 +127,33 @@ int paged_attn_decode_fused(const void *q, const void *k_cache, const void *v_ca
                             int partition_size, void *out, float *max_logits, float *exp_sums,
                             float *tmp_out, int max_num_partitions, int32_t *counters,
                             void *stream);
+
+/*
+ * paged_attn_decode_fused without allocation, for callers that cannot call
+ * hipMalloc or take a workspace from an allocator (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * computation, inputs, output (`out` for every sequence, zero rows for
+ * zero-length sequences) and schedule as paged_attn_decode_fused with
+ * max_num_partitions = paged_attn_num_partitions(max_blocks_per_seq,
+ * block_size, partition_size); its workspace (partial records and arrival
+ * counters) is instead a fixed 64 MiB device array inside the library, one
+ * per GPU the library runs on, held until the process ends.  Limits: the
+ * records, num_seqs * H_q * max_num_partitions * (D + 2) fp32 values in
+ * 256-byte aligned sections, must fit in 64 MiB less 256 KiB of counters, and
+ * num_seqs * H_kv <= 65536; beyond either the call returns
+ * PA_ERR_SCRATCH_LIMIT without launching anything (a larger partition_size
+ * needs fewer records).  The first call on a device takes the array's device
+ * address and clears its counters (a fill kernel on `stream`); no call
+ * allocates or frees memory.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give wrong results; calls ordered on one stream are safe.
+ * Errors: as paged_attn_decode_fused, plus PA_ERR_SCRATCH_LIMIT.
+ */
+int paged_attn_decode_fused_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *seq_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, int max_blocks_per_seq,
+                                    float scale, int partition_size, void *out, void *stream);
 
 /*
  * Paged GQA decode over an FP8 KV cache (the B200 page, "Stage D: FP8 Paged KV

@@ -30,6 +30,7 @@ PA_ERR_UNSUPPORTED = 3
 PA_ERR_LAUNCH = 4
 PA_ERR_ALIGNMENT = 5
 PA_ERR_BAD_VALUE = 6
+PA_ERR_SCRATCH_LIMIT = 7
 
 
 class PagedAttnError(RuntimeError):
@@ -54,6 +55,7 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIBRARY)
         lib.paged_attn_decode.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp]
         lib.paged_attn_decode_fused.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp, _vp]
+        lib.paged_attn_decode_fused_noalloc.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _i, _vp, _vp]
         lib.paged_attn_decode_reduce.argtypes = [_vp] * 4 + [_i] * 5 + [_vp, _vp]
         lib.paged_attn_decode_fp8.argtypes = [_vp] * 7 + [_i] * 7 + [ctypes.c_float, _i] + [_vp] * 4 + [_i, _vp]
         lib.paged_attn_kv_append.argtypes = [_vp] * 5 + [_i] * 8 + [_vp] * 3
@@ -74,7 +76,8 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_read_probe.argtypes = [_vp, ctypes.c_longlong, _vp, _i, _vp]
         lib.paged_attn_status_string.argtypes = [_i]
         lib.paged_attn_status_string.restype = ctypes.c_char_p
-        for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_reduce",
+        for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_fused_noalloc",
+                   "paged_attn_decode_reduce",
                    "paged_attn_decode_fp8", "paged_attn_kv_append", "paged_attn_kv_append_fp8",
                    "paged_attn_decode_xpacked", "paged_attn_kv_append_xpacked",
                    "paged_attn_decode_tokens", "paged_attn_decode_reduce_indptr",
@@ -210,6 +213,29 @@ def paged_attn_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale: 
         _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), tmp_out.shape[2],
         _ptr(counters), _stream(stream))
     _check("paged_attn_decode_fused", st)
+
+
+def paged_attn_decode_fused_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                                    partition_size: int, out, stream=None) -> None:
+    """paged_attn_decode_fused with the library's fixed device scratch as its
+    workspace: allocates nothing (calls that overlap on one GPU race)."""
+    import torch
+    _want(q, torch.bfloat16, "q")
+    _want(k_cache, torch.bfloat16, "k_cache")
+    _want(v_cache, torch.bfloat16, "v_cache")
+    _want(block_tables, torch.int32, "block_tables")
+    _want(seq_lens, torch.int32, "seq_lens")
+    _want(out, torch.bfloat16, "out")
+    num_seqs, hq, d = q.shape
+    num_blocks, hkv, bs, _ = k_cache.shape
+    _shape(v_cache, k_cache.shape, "v_cache", "paged_attn_decode_fused_noalloc")
+    _check_decode_buffers("paged_attn_decode_fused_noalloc", q, seq_lens, block_tables, out, 0,
+                          None, None, None, 1)
+    st = library().paged_attn_decode_fused_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), num_seqs, hq,
+        hkv, d, bs, num_blocks, block_tables.shape[1], float(scale), int(partition_size), _ptr(out),
+        _stream(stream))
+    _check("paged_attn_decode_fused_noalloc", st)
 
 
 def paged_attn_decode_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: int, out,

@@ -5,6 +5,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "pa_launch.h"
 #include "paged_attn.h"
 
@@ -68,6 +70,7 @@ const char *paged_attn_status_string(int status) {
         case PA_ERR_LAUNCH: return "kernel launch failed";
         case PA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
         case PA_ERR_BAD_VALUE: return "scale must be positive and finite";
+        case PA_ERR_SCRATCH_LIMIT: return "problem larger than the library's fixed scratch (no-allocation entry point)";
         default: return "unknown status";
     }
 }
@@ -287,6 +290,79 @@ int paged_attn_decode_fused(const void *q, const void *k_cache, const void *v_ca
                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
                          partition_size, out, max_logits, exp_sums, tmp_out, max_num_partitions,
                          counters, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode with the library's own fixed scratch, for callers that cannot
+// allocate (graph capture, tight serving loops, harnesses that forbid it).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr long long kNoallocScratchBytes = 64LL << 20;      // per device, for the process lifetime
+constexpr long long kNoallocMaxPairs = 1LL << 16;           // (sequence, kv head) arrival counters
+constexpr long long kNoallocCounterBytes = kNoallocMaxPairs * 4;
+
+// The workspace of paged_attn_decode_fused_noalloc: the arrival counters
+// (kNoallocMaxPairs int32 at offset 0, zero between calls: every completed
+// fused launch leaves the counters it used at zero), then the partial records
+// of the current call.  In host code `scratch` names a host-side stand-in:
+// only the device address taken at set-up is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::atomic<unsigned char *> g_scratch_dev[pa::kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Device address of the current device's `scratch`, set up once per device
+// (the counters cleared by a fill kernel on `stream`, ahead of the first
+// decode launch on it); null if the address cannot be taken.
+unsigned char *noalloc_scratch(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= pa::kMaxDevices) return nullptr;
+    unsigned char *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = static_cast<unsigned char *>(addr);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, reinterpret_cast<uint32_t *>(p),
+                       (int)kNoallocMaxPairs);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch_dev[dev].store(p, std::memory_order_release);
+    return p;
+}
+}  // namespace
+
+int paged_attn_decode_fused_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *seq_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, int max_blocks_per_seq,
+                                    float scale, int partition_size, void *out, void *stream) {
+    int st = check_common(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq);
+    if (st != PA_OK) return st;
+    if (!out) return PA_ERR_NULL_POINTER;
+    if (!scale_ok(scale)) return PA_ERR_BAD_VALUE;
+    if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_BAD_SHAPE;
+    const int nparts = paged_attn_num_partitions(max_blocks_per_seq, block_size, partition_size);
+    if (nparts <= 0) return PA_ERR_BAD_SHAPE;
+    // scratch layout: counters | max_logits | exp_sums | tmp_out (256-byte aligned sections)
+    const long long rows = (long long)num_seqs * num_q_heads * nparts;
+    const long long off_ml = kNoallocCounterBytes;
+    const long long off_es = off_ml + round_up(rows * 4, 256);
+    const long long off_to = off_es + round_up(rows * 4, 256);
+    const long long need = off_to + rows * head_dim * 4;
+    if ((long long)num_seqs * num_kv_heads > kNoallocMaxPairs || need > kNoallocScratchBytes)
+        return PA_ERR_SCRATCH_LIMIT;
+    if (num_seqs == 0) return PA_OK;
+    unsigned char *base = noalloc_scratch(static_cast<hipStream_t>(stream));
+    if (!base) return PA_ERR_LAUNCH;
+    return paged_attn_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                   num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                   scale, partition_size, out, reinterpret_cast<float *>(base + off_ml),
+                                   reinterpret_cast<float *>(base + off_es),
+                                   reinterpret_cast<float *>(base + off_to), nparts,
+                                   reinterpret_cast<int32_t *>(base), stream);
 }
 
 namespace {

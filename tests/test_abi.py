@@ -30,14 +30,15 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_prefill_tile_map", "paged_attn_status_string", "paged_attn_decode_fp8",
         "paged_attn_kv_append", "paged_attn_kv_append_fp8", "paged_attn_decode_xpacked",
         "paged_attn_kv_append_xpacked", "paged_attn_decode_tokens",
-        "paged_attn_decode_reduce_indptr", "paged_attn_read_probe"}
+        "paged_attn_decode_reduce_indptr", "paged_attn_read_probe",
+        "paged_attn_decode_fused_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_status_strings(lib):
     assert pa.status_string(0) == "ok"
-    for code in range(1, 7):
+    for code in range(1, 8):
         assert pa.status_string(code) not in ("ok", "unknown status")
     assert pa.status_string(99) == "unknown status"
 
@@ -462,3 +463,27 @@ def test_decode_binding_checks_partial_shapes(lib, bad):
     with pytest.raises(ValueError):
         pa.paged_attn_decode_reduce(t["ml"], t["es"], t["to"], t["sl"], 16, t["out"])
 
+
+def _noalloc_call(lib, S, Hq, Hkv, D, mbps, P, ptr=16):
+    return lib.paged_attn_decode_fused_noalloc(ptr, ptr, ptr, ptr, ptr, S, Hq, Hkv, D, 16, 8, mbps,
+                                               0.125, P, ptr, None)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D,mbps,P,why", [
+    (32, 32, 8, 128, 3000, 16, "records of 3000 partitions x 1024 rows exceed 64 MiB"),
+    (256, 64, 8, 128, 2048, 1024, "the large ragged batch at P = 1024 (272 MB of records)"),
+    (32769, 2, 2, 64, 1, 16, "more (sequence, kv head) pairs than counters"),
+])
+def test_noalloc_rejects_problems_beyond_its_scratch(lib, S, Hq, Hkv, D, mbps, P, why):
+    """Rejected on the host before anything touches a device (dummy pointers)."""
+    assert _noalloc_call(lib, S, Hq, Hkv, D, mbps, P) == pa.PA_ERR_SCRATCH_LIMIT, why
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(P=0), pa.PA_ERR_BAD_SHAPE), (dict(P=24), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED), (dict(ptr=8), pa.PA_ERR_ALIGNMENT),
+])
+def test_noalloc_validation(lib, over, status):
+    a = dict(S=4, Hq=8, Hkv=2, D=64, mbps=3, P=16, ptr=16)
+    a.update(over)
+    assert _noalloc_call(lib, **a) == status
