@@ -141,9 +141,28 @@ def to_fp8_cache(pa, case, d):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on host cores, bounded sample
 # ---------------------------------------------------------------------------
+def host_cpu():
+    """nproc (CPUs this process may run on), the machine's logical CPU count
+    and the CPU model name, as the host reports them."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count()
+    return {"nproc": nproc, "logical_cpus": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(case, seconds: float, prefill: bool):
     import oracle
     orc = oracle.get()
+    host = host_cpu()
     if prefill:
         t0 = time.perf_counter()
         orc.prefill_case(case)
@@ -153,7 +172,7 @@ def cpu_baseline(case, seconds: float, prefill: bool):
         c = case.seq_lens - n
         flops = 4.0 * case.head_dim * case.num_q_heads * float(np.sum(n * c + n * (n + 1) / 2))
         return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
-                "kind": "oracle",
+                "kind": "oracle", **host,
                 "sample": f"one full pass of the {case.name} workload ({case.total_q} query rows), "
                           f"{dt:.1f} s wall"}
     P = case.partition_size
@@ -169,7 +188,7 @@ def cpu_baseline(case, seconds: float, prefill: bool):
         reps += 1
     what = "partials + merge" if P else "single-pass decode"
     return {"value": case.kv_tokens * reps / t_total, "unit": "KV tokens/s",
-            "cores": orc.num_threads(), "kind": "oracle",
+            "cores": orc.num_threads(), "kind": "oracle", **host,
             "sample": f"the full {case.name} workload ({case.num_seqs} sequences, {case.kv_tokens} KV "
                       f"tokens), oracle {what}, repeated {reps}x in {t_total:.1f} s"}
 
@@ -177,7 +196,10 @@ def cpu_baseline(case, seconds: float, prefill: bool):
 # ---------------------------------------------------------------------------
 # runs
 # ---------------------------------------------------------------------------
-def run_decode(args, pa):
+def run_decode(args, pa, passes=("fused", "dist", "ceiling")):
+    """The decode step of args.workload, timed cold over rotated pool copies;
+    `passes` adds the fused entry point's step, the step-time distribution and
+    warm case, and the read / gather ceilings."""
     import numpy as np
     import torch
     copies = args.copies or (3 if args.workload == "llama3_8b_decode" else 2)
@@ -293,7 +315,7 @@ def run_decode(args, pa):
     # timed region 3 (bf16 block cache, separate merge timed above): the same
     # steps through the fused entry point, reported beside the main line
     ms_fused = None
-    if P and not (fused or fp8 or xp or tok):
+    if P and "fused" in passes and not (fused or fp8 or xp or tok):
         def fused_step(i):
             d = devs[i % copies]
             pa.paged_attn_decode_fused(d["q"], d["k"], d["v"], d["bt"], d["sl"], scale, P, out,
@@ -319,8 +341,10 @@ def run_decode(args, pa):
             evs[i + 1].record(stream)
         torch.cuda.synchronize()
         return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n)])
-    dist = per_step(step, max(args.steps, 100))
-    warm = per_step(lambda i: step(0), max(args.steps, 100))
+    dist = warm = None
+    if "dist" in passes:
+        dist = per_step(step, max(args.steps, 100))
+        warm = per_step(lambda i: step(0), max(args.steps, 100))
     # leave the output of a full step behind (the partials above are not merged)
     step(0)
     torch.cuda.synchronize()
@@ -334,7 +358,7 @@ def run_decode(args, pa):
     kern_gbps = kv_bytes / (ms_kernel * 1e-3) / 1e9
     traffic = counter_traffic("decode_fp8" if fp8 else "decode_xpacked" if xp else "decode",
                               DECODE_SOURCE, args.workload)
-    ceiling = None if args.no_read_ceiling else read_ceiling(pa, kv_bytes, copies)
+    ceiling = None if (args.no_read_ceiling or "ceiling" not in passes) else read_ceiling(pa, kv_bytes, copies, cases, devs)
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -383,12 +407,16 @@ def run_decode(args, pa):
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
-    result["step_distribution"] = {
-        "per_step_events": int(dist.size), "median_ms": float(np.median(dist)),
-        "p10_ms": float(np.percentile(dist, 10)), "p90_ms": float(np.percentile(dist, 90)),
-        "warm_one_copy_median_ms": float(np.median(warm)),
-        "note": "an event between consecutive steps (timed separately from ms_per_step); warm = the "
-                "same pool copy every step, so part of it stays in the 256 MB Infinity Cache"}
+    if args.cold_only:
+        result["cold_only"] = ("only the warmup, the timed steps and the partition kernel's own timed "
+                               "launches ran, every one on a rotated (cold) pool copy")
+    if dist is not None:
+        result["step_distribution"] = {
+            "per_step_events": int(dist.size), "median_ms": float(np.median(dist)),
+            "p10_ms": float(np.percentile(dist, 10)), "p90_ms": float(np.percentile(dist, 90)),
+            "warm_one_copy_median_ms": float(np.median(warm)),
+            "note": "an event between consecutive steps (timed separately from ms_per_step); warm = the "
+                    "same pool copy every step, so part of it stays in the 256 MB Infinity Cache"}
     if ms_fused is not None:
         result["fused_merge"] = {
             "entry_point": "paged_attn_decode_fused (stream-K schedule, merge in the last workgroup)",
@@ -398,15 +426,70 @@ def run_decode(args, pa):
     if ceiling is not None:
         ceiling["kernel_frac_of_same_bytes_read"] = kern_gbps / ceiling["same_bytes_rotated_gbps"]
         ceiling["kernel_frac_of_large_read"] = kern_gbps / ceiling["large_buffer_gbps"]
+        if "gather_tiles_gbps" in ceiling:
+            ceiling["kernel_frac_of_tile_gather"] = kern_gbps / ceiling["gather_tiles_gbps"]
+            ceiling["step_frac_of_tile_gather"] = step_gbps / ceiling["gather_tiles_gbps"]
         result["read_ceiling"] = ceiling
     return result, cases[0]
 
 
-def read_ceiling(pa, nbytes: int, copies: int):
+def gather_ceiling(pa, cases, devs):
+    """Paged-gather ceiling from the library's gather probe: the decode's own
+    K/V tiles of the rotated pool copies, read through their block tables,
+    best over grids of 1..32 workgroups per CU; per-(kv head, block) tiles in
+    the decode's order, and whole blocks (all kv heads of a block together)."""
+    import numpy as np
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    c0 = cases[0]
+    if c0.num_seqs > 1024 or c0.head_dim not in (64, 128, 256):
+        return {}
+    pref = np.zeros(c0.num_seqs + 1, np.int32)
+    pref[1:] = np.cumsum((c0.seq_lens.astype(np.int64) + 15) // 16)
+    prefd = torch.from_numpy(pref).cuda()
+    nbytes = int(pref[-1]) * c0.num_kv_heads * 2 * 16 * c0.head_dim * 2
+    out = {}
+    for whole in (False, True):
+        best = None
+        for m in (1, 2, 4, 8, 16, 32):
+            partial = torch.empty(m * cus, dtype=torch.int32, device="cuda")
+            call = lambda i: pa.paged_attn_gather_probe(devs[i % len(devs)]["k"], devs[i % len(devs)]["v"],
+                                                        devs[i % len(devs)]["bt"], prefd, whole, partial,
+                                                        stream=stream)
+            for i in range(3):
+                call(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 30
+            e0.record(stream)
+            for i in range(reps):
+                call(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            if best is None or ms < best[0]:
+                best = (ms, m * cus)
+        key = "gather_blocks" if whole else "gather_tiles"
+        out[key + "_gbps"] = nbytes / (best[0] * 1e-3) / 1e9
+        out[key + "_ms"] = best[0]
+        out[key + "_workgroups"] = best[1]
+    out["gather_bytes"] = nbytes
+    out["gather_probe"] = ("paged_attn_gather_probe over the decode's rotated pool copies: tiles = the K and V "
+                           "tile of one (sequence, kv head, block) per wave in the decode's order; blocks = "
+                           "consecutive waves read one block's H_kv tiles of K then V; best of 1..32 "
+                           "workgroups per CU")
+    log(f"gather ceiling: tiles {out['gather_tiles_gbps']:.0f} GB/s ({out['gather_tiles_ms'] * 1e3:.1f} us), "
+        f"whole blocks {out['gather_blocks_gbps']:.0f} GB/s ({out['gather_blocks_ms'] * 1e3:.1f} us)")
+    return out
+
+
+def read_ceiling(pa, nbytes: int, copies: int, cases=None, devs=None):
     """Measured HBM read ceiling from the library's read-stream probe: the best
     rate over grids of 16..256 workgroups per CU, on one large buffer (steady
     streaming) and on `copies` rotated buffers of `nbytes` each (the decode's
-    own bytes per launch, read cold)."""
+    own bytes per launch, read cold); plus, given the decode's pool copies,
+    the paged-gather ceiling of its own tiles."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
@@ -437,11 +520,14 @@ def read_ceiling(pa, nbytes: int, copies: int):
     log(f"read ceiling: {large_gbps:.0f} GB/s over 4 GiB ({large_nwg} workgroups), {same_gbps:.0f} GB/s "
         f"over {copies} rotated buffers of {nbytes / 1e6:.1f} MB ({same_ms * 1e3:.1f} us each, "
         f"{same_nwg} workgroups)")
-    return {"probe": "paged_attn_read_probe (16-byte nontemporal loads, XOR-folded), best of "
-                     "16..256 workgroups per CU",
-            "large_buffer_bytes": 1 << 32, "large_buffer_gbps": large_gbps, "large_buffer_workgroups": large_nwg,
-            "same_bytes": nbytes, "same_bytes_rotated_copies": copies,
-            "same_bytes_rotated_gbps": same_gbps, "same_bytes_ms": same_ms, "same_bytes_workgroups": same_nwg}
+    res = {"probe": "paged_attn_read_probe (16-byte nontemporal loads, XOR-folded), best of "
+                    "16..256 workgroups per CU",
+           "large_buffer_bytes": 1 << 32, "large_buffer_gbps": large_gbps, "large_buffer_workgroups": large_nwg,
+           "same_bytes": nbytes, "same_bytes_rotated_copies": copies,
+           "same_bytes_rotated_gbps": same_gbps, "same_bytes_ms": same_ms, "same_bytes_workgroups": same_nwg}
+    if cases is not None and devs is not None:
+        res.update(gather_ceiling(pa, cases, devs))
+    return res
 
 
 def run_prefill(args, pa):
@@ -569,6 +655,41 @@ def run_append(args, pa):
     }, None
 
 
+def secondary_lines(args, pa):
+    """The other configurations, timed in the same run as the headline line
+    (no CPU baseline for them): the long-context split-KV and large ragged
+    decode (separate merge and fused entry point) and the ragged prefill."""
+    import torch
+    out = {}
+    t0 = time.perf_counter()
+    for wl in ("long_split_decode", "large_ragged_decode"):
+        sub = argparse.Namespace(**vars(args))
+        sub.workload, sub.steps, sub.warmup, sub.cold_only = wl, args.secondary_steps, 5, False
+        sub.kv_dtype, sub.kv_layout, sub.merge, sub.partition_size, sub.copies = "bf16", "tile", "separate", None, None
+        r, _ = run_decode(sub, pa, passes=("fused",))
+        rf = r["roofline"]
+        out[wl] = {"ms_per_step": r["ms_per_step"], "kv_tokens_per_s": r["value"],
+                   "hbm_gbps": r["hbm_gbps"], "hbm_pct_of_peak": r["hbm_pct_of_peak"],
+                   "partition_kernel_ms": rf["kernel_ms"], "partition_kernel_frac": rf["frac"],
+                   "partition_size": r["config"]["partition_size"], "kv_tokens": r["config"]["kv_tokens"],
+                   "pool_copies_rotated": r["config"]["kv_pool_copies_rotated"], "steps": sub.steps}
+        if "fused_merge" in r:
+            out[wl]["fused_ms_per_step"] = r["fused_merge"]["ms_per_step"]
+            out[wl]["fused_kv_tokens_per_s"] = r["fused_merge"]["value"]
+            out[wl]["fused_frac_of_peak"] = r["fused_merge"]["frac_of_peak"]
+        torch.cuda.empty_cache()
+    sub = argparse.Namespace(**vars(args))
+    sub.workload, sub.steps, sub.warmup, sub.prefill_form = "ragged_prefill", args.secondary_steps, 5, "split"
+    r, _ = run_prefill(sub, pa)
+    out["ragged_prefill"] = {"ms_per_step": r["ms_per_step"], "tflops": r["value"],
+                             "frac_of_bf16_peak": r["roofline"]["frac"], "kv_chunk": r["config"]["kv_chunk"],
+                             "total_q": r["config"]["total_q"], "steps": sub.steps}
+    torch.cuda.empty_cache()
+    out["note"] = (f"timed in this run after the headline ({args.secondary_steps} steps each, cold rotated "
+                   f"pool copies for decode; {time.perf_counter() - t0:.0f} s including input generation)")
+    return out
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -609,6 +730,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the read-stream probe that measures the HBM read ceiling (decode workloads)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only the warmup and the timed cold steps (plus the partition kernel's own timed "
+                         "launches): no fused, per-step, warm, ceiling, secondary or CPU passes -- the mode "
+                         "whose rocprofv3 traces match the line")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary configurations the default decode line carries")
+    ap.add_argument("--secondary-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (the reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -633,8 +761,13 @@ def main():
     elif args.workload == "kv_append":
         result, case = run_append(args, pa)
     else:
-        result, case = run_decode(args, pa)
-    if not args.no_cpu_baseline and case is not None and args.kv_dtype == "bf16" and args.kv_layout == "tile":
+        result, case = run_decode(args, pa, passes=() if args.cold_only else ("fused", "dist", "ceiling"))
+    if (args.workload == "llama3_8b_decode" and not (args.cold_only or args.no_secondary)
+            and args.kv_dtype == "bf16" and args.kv_layout == "tile" and args.merge == "separate"):
+        log("timing the secondary configurations")
+        result["secondary"] = secondary_lines(args, pa)
+    if (not (args.no_cpu_baseline or args.cold_only) and case is not None and args.kv_dtype == "bf16"
+            and args.kv_layout == "tile"):
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, args.workload == "ragged_prefill")
     else:

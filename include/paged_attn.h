@@ -388,6 +388,41 @@ int paged_attn_prefill_tile_map(const int32_t *cu_seqlens_host, int num_seqs, in
 int paged_attn_read_probe(const void *buf, long long bytes, uint32_t *partial, int num_workgroups,
                           void *stream);
 
+/*
+ * Paged-gather read probe: a measurement helper beside the attention path,
+ * not a step of it.  It reads exactly the K/V bytes one paged_attn_decode
+ * of the batch reads -- every (block, kv head) tile of every used logical
+ * block of every sequence, tail slots included -- through block_tables, with
+ * the decode's 16-byte nontemporal loads, and nothing else, so it measures
+ * the rate at which a paged cache can be gathered (the BI-V100 page, section
+ * 3 "Paged K/V Gather", counts the gather's memory accesses; this times
+ * them).  A piece is two 16 * head_dim * 2-byte tiles read by one wave,
+ * two pieces in flight:
+ *   whole_blocks 0: the K tile and the V tile of one (sequence, kv head,
+ *                   block), pieces in (sequence, kv head, block) order -- the
+ *                   decode's own walk over scattered tiles;
+ *   whole_blocks 1: consecutive tile pairs of [K block | V block] of one
+ *                   (sequence, block) -- each block's contiguous
+ *                   H_kv * 16 * head_dim K and V rows read together.
+ * Both modes read the same bytes.  The grid's waves split the pieces into
+ * equal consecutive runs.  partial[w] receives the XOR of the 32-bit words
+ * workgroup w read; the XOR over all entries equals the XOR of every 32-bit
+ * word of the K and V tiles of the used blocks (a block used twice cancels).
+ *   k_cache, v_cache  bf16 [num_blocks, H_kv, block_size, head_dim], device,
+ *                     16-byte aligned, read only.
+ *   block_tables      int32 [num_seqs, max_blocks_per_seq], device.
+ *   block_prefix      int32 [num_seqs + 1], device: block_prefix[0] = 0 and
+ *                     block_prefix[s + 1] - block_prefix[s] = ceil(L_s / 16).
+ *   partial           uint32 [num_workgroups], device, written only.
+ * Limits: num_seqs <= 1024, head_dim in {64, 128, 256}, block_size 16.
+ * Errors: PA_ERR_NULL_POINTER, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_ALIGNMENT, PA_ERR_LAUNCH.  Enqueued on `stream`.
+ */
+int paged_attn_gather_probe(const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                            const int32_t *block_prefix, int num_seqs, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int whole_blocks, uint32_t *partial,
+                            int num_workgroups, void *stream);
+
 /* Human-readable name of a status code. */
 const char *paged_attn_status_string(int status);
 

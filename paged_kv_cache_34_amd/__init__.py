@@ -74,6 +74,7 @@ def library() -> ctypes.CDLL:
         lib.paged_attn_choose_partition_size.argtypes = [_i, _i, _i, ctypes.c_long]
         lib.paged_attn_prefill_tile_map.argtypes = [_vp, _i, _i, _vp, _vp, _i]
         lib.paged_attn_read_probe.argtypes = [_vp, ctypes.c_longlong, _vp, _i, _vp]
+        lib.paged_attn_gather_probe.argtypes = [_vp] * 4 + [_i] * 6 + [_vp, _i, _vp]
         lib.paged_attn_status_string.argtypes = [_i]
         lib.paged_attn_status_string.restype = ctypes.c_char_p
         for fn in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_decode_fused_noalloc",
@@ -84,7 +85,7 @@ def library() -> ctypes.CDLL:
                    "paged_attn_prefill_ragged", "paged_attn_prefill_ragged_split",
                    "paged_attn_prefill_chunk_size",
                    "paged_attn_num_partitions", "paged_attn_choose_partition_size",
-                   "paged_attn_prefill_tile_map", "paged_attn_read_probe"):
+                   "paged_attn_prefill_tile_map", "paged_attn_read_probe", "paged_attn_gather_probe"):
             getattr(lib, fn).restype = _i
         _lib = lib
     return _lib
@@ -547,6 +548,30 @@ def paged_attn_read_probe(buf, partial, stream=None) -> None:
     nbytes = buf.numel() * buf.element_size()
     _check("paged_attn_read_probe",
            library().paged_attn_read_probe(_ptr(buf), nbytes, _ptr(partial), partial.numel(), _stream(stream)))
+
+
+def paged_attn_gather_probe(k_cache, v_cache, block_tables, block_prefix, whole_blocks: bool, partial,
+                            stream=None) -> None:
+    """Paged-gather read probe over the K/V tiles a decode of the batch reads
+    (block_prefix int32 [num_seqs + 1]: prefix sums of ceil(L / 16)); one
+    workgroup per element of the int32 tensor `partial`, which receives each
+    workgroup's XOR of the 32-bit words it read."""
+    import torch
+    _want(k_cache, torch.bfloat16, "k_cache")
+    _want(v_cache, torch.bfloat16, "v_cache")
+    _want(block_tables, torch.int32, "block_tables")
+    _want(block_prefix, torch.int32, "block_prefix")
+    _want(partial, torch.int32, "partial")
+    num_blocks, hkv, bs, d = k_cache.shape
+    _shape(v_cache, k_cache.shape, "v_cache", "paged_attn_gather_probe")
+    num_seqs = block_tables.shape[0]
+    if block_prefix.numel() != num_seqs + 1:
+        raise ValueError(f"paged_attn_gather_probe: block_prefix must have {num_seqs + 1} entries")
+    _check("paged_attn_gather_probe",
+           library().paged_attn_gather_probe(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                             _ptr(block_prefix), num_seqs, hkv, d, bs, block_tables.shape[1],
+                                             int(bool(whole_blocks)), _ptr(partial), partial.numel(),
+                                             _stream(stream)))
 
 
 def paged_attn_status_string(status: int) -> str:

@@ -265,6 +265,22 @@ int paged_attn_read_probe(const void *buf, long long bytes, uint32_t *partial, i
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int paged_attn_gather_probe(const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                            const int32_t *block_prefix, int num_seqs, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int whole_blocks, uint32_t *partial,
+                            int num_workgroups, void *stream) {
+    if (!k_cache || !v_cache || !block_tables || !block_prefix || !partial) return PA_ERR_NULL_POINTER;
+    if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_workgroups <= 0 ||
+        (whole_blocks != 0 && whole_blocks != 1))
+        return PA_ERR_BAD_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize || num_seqs > 1024) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGNMENT;
+    const hipError_t e = pa::launch_gather_probe(k_cache, v_cache, block_tables, block_prefix, num_seqs,
+                                                 num_kv_heads, head_dim, max_blocks_per_seq, whole_blocks,
+                                                 partial, num_workgroups, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, int num_seqs,
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,

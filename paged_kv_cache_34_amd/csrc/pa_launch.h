@@ -125,6 +125,10 @@ hipError_t launch_prefill(const PrefillArgs &a);
 hipError_t launch_kv_append(const AppendArgs &a);
 hipError_t launch_kv_append_fp8(const AppendArgs &a);
 hipError_t launch_kv_append_xpacked(const AppendArgs &a);
+hipError_t launch_gather_probe(const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                               const int32_t *block_prefix, int num_seqs, int num_kv_heads, int head_dim,
+                               int max_blocks_per_seq, int whole_blocks, uint32_t *partial, int num_workgroups,
+                               hipStream_t stream);
 hipError_t launch_read_probe(const void *buf, long long bytes, uint32_t *partial, int num_workgroups,
                              hipStream_t stream);
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
         "paged_attn_kv_append", "paged_attn_kv_append_fp8", "paged_attn_decode_xpacked",
         "paged_attn_kv_append_xpacked", "paged_attn_decode_tokens",
         "paged_attn_decode_reduce_indptr", "paged_attn_read_probe",
-        "paged_attn_decode_fused_noalloc"}
+        "paged_attn_decode_fused_noalloc", "paged_attn_gather_probe"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -487,3 +487,16 @@ def test_noalloc_validation(lib, over, status):
     a = dict(S=4, Hq=8, Hkv=2, D=64, mbps=3, P=16, ptr=16)
     a.update(over)
     assert _noalloc_call(lib, **a) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=None), pa.PA_ERR_NULL_POINTER), (dict(pref=None), pa.PA_ERR_NULL_POINTER),
+    (dict(S=0), pa.PA_ERR_BAD_SHAPE), (dict(nwg=0), pa.PA_ERR_BAD_SHAPE), (dict(whole=2), pa.PA_ERR_BAD_SHAPE),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED), (dict(bs=32), pa.PA_ERR_UNSUPPORTED), (dict(S=1025), pa.PA_ERR_UNSUPPORTED),
+    (dict(k=8), pa.PA_ERR_ALIGNMENT),
+])
+def test_gather_probe_validation(lib, over, status):
+    a = dict(k=16, v=16, bt=16, pref=16, S=4, hkv=2, D=64, bs=16, mbps=3, whole=0, part=16, nwg=4)
+    a.update(over)
+    assert lib.paged_attn_gather_probe(a["k"], a["v"], a["bt"], a["pref"], a["S"], a["hkv"], a["D"], a["bs"],
+                                       a["mbps"], a["whole"], a["part"], a["nwg"], None) == status

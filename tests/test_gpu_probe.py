@@ -41,3 +41,39 @@ def test_read_probe_status_through_binding():
     partial = t.zeros(4, dtype=t.int32, device="cuda")
     with pytest.raises(pa.PagedAttnError):
         pa.paged_attn_read_probe(buf, partial)
+
+
+def used_tiles_xor(case) -> int:
+    """XOR of every 32-bit word of the K and V tiles of the blocks each
+    sequence uses (ceil(L / 16) logical blocks, all kv heads), on the host."""
+    acc = 0
+    for s, L in enumerate(case.seq_lens):
+        nb = (int(L) + 15) // 16
+        for blk in case.block_tables[s, :nb]:
+            for pool in (case.k_cache, case.v_cache):
+                acc ^= host_xor(np.ascontiguousarray(pool[int(blk)]).view(np.uint32).ravel())
+    return acc
+
+
+@pytest.mark.parametrize("lens,hkv,D,nwg", [
+    ([1, 37, 100], 1, 64, 1),
+    ([16, 17, 511, 2000], 2, 128, 3),
+    ([700, 1, 4096, 33], 8, 128, 64),
+    ([300, 1000], 4, 256, 512),
+    ([5] * 40, 3, 64, 7),            # odd kv head count: a piece straddles K and V
+])
+@pytest.mark.parametrize("whole", [False, True])
+def test_gather_probe_xor(lens, hkv, D, nwg, whole):
+    import workloads
+    t = torch()
+    case = workloads.build_case("gather_probe", 900 + D + hkv, lens, hkv, hkv, D)
+    announce(f"gather probe: lens={lens} H_kv={hkv} D={D} grid={nwg} whole_blocks={whole}")
+    pref = np.zeros(len(lens) + 1, np.int32)
+    pref[1:] = np.cumsum([(int(L) + 15) // 16 for L in case.seq_lens])
+    k = t.from_numpy(case.k_cache.view(np.int16)).view(t.bfloat16).cuda()
+    v = t.from_numpy(case.v_cache.view(np.int16)).view(t.bfloat16).cuda()
+    partial = t.full((nwg,), -1, dtype=t.int32, device="cuda")
+    pa.paged_attn_gather_probe(k, v, t.from_numpy(case.block_tables).cuda(), t.from_numpy(pref).cuda(),
+                               whole, partial)
+    t.cuda.synchronize()
+    assert host_xor(partial.cpu().numpy()) == used_tiles_xor(case)
