@@ -15,10 +15,10 @@
 //     one workgroup of NW waves that take the partition's 16-token blocks
 //     round-robin, so one K/V load serves all G query heads of the kv head;
 //   * QK^T of a block is v_mfma_f32_16x16x32_bf16 with the block's K tile as
-//     the A operand and the G query rows as the B operand; a row-major bf16 K
-//     tile is loaded in contiguous 1 KB runs of whole rows and passes through
-//     the wave's LDS stage on its way into the operand layout (the x-packed and
-//     FP8 tiles load straight into it); the result S^T leaves lane l with the
+//     the A operand and the G query rows as the B operand; a row-major K tile
+//     (bf16, or FP8 codes) is loaded in contiguous 1 KB runs of whole rows and
+//     passes through the wave's LDS stage on its way into the operand layout
+//     (an x-packed tile loads straight into it); the result S^T leaves lane l with the
 //     scores of head l % 16 for 4 tokens;
 //   * the online softmax runs on that layout: per-head block max over the 4
 //     lane groups with permlane swaps, a lazy running max (rescale only when a
@@ -138,7 +138,7 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // (col = lane % 16, grp = lane / 16):
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = the K tile, lane: token
 //                  col, 16-byte chunk 4j + grp, read from the wave's LDS stage
-//                  (row-major bf16) or loaded so (x-packed, FP8); B = the
+//                  (row-major) or loaded so (x-packed); B = the
 //                  query rows) -> lane holds scores of head col for tokens
 //                  4 grp + i;
 //   online softmax per head (block max over the 4 lane groups with permlane
@@ -267,7 +267,7 @@ __device__ __forceinline__ void lds_barrier() {
 // (col = lane % 16, grp = lane / 16):
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = the K tile, lane: token
 //                  col, 16-byte chunk 4j + grp, read from the wave's LDS stage
-//                  (row-major bf16) or loaded so (x-packed, FP8); B = the
+//                  (row-major) or loaded so (x-packed); B = the
 //                  query rows) -> lane holds scores of head col for tokens
 //                  4 grp + i;
 //   online softmax per head (block max over the 4 lane groups with permlane
@@ -340,10 +340,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     // each lane reads its MFMA operand; loading the operand layout directly
     // would make every instruction touch 16 rows in 64-byte pieces, which
     // measured ~3% slower on MI355X.
-    constexpr bool KST = !FP8 && !XP && !TOK;
+    // (An FP8 tile likewise, its codes staged as bytes and converted after the
+    // operand read.)
+    constexpr bool KST = !XP && !TOK;
     const int v_voff = XP ? col * 32 + 8 * grp : (vrow * D * EB) + vcol * 16;
-    const int k_voff = FP8 ? col * D + 16 * grp : XP ? (grp * 16 + col) * 16 : v_voff;
-    constexpr int K_STEP = XP || KST ? 1024 : 64;  // bytes between a lane's K loads
+    const int k_voff = XP ? (grp * 16 + col) * 16 : v_voff;
+    constexpr int K_STEP = 1024;  // bytes between a lane's K loads (one whole-row run each)
     // FP8 scales: [num_blocks, H_kv, 16] floats, the lane's 4 score tokens 4 grp + 0..3
     const float *ks_cur = FP8 ? prm.k_scales + kvh * kBlock : nullptr;
     const float *vs_cur = FP8 ? prm.v_scales + kvh * kBlock : nullptr;
@@ -442,14 +444,18 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         // K through the wave's stage first (row-major bf16): rows as loaded,
         // then the QK^T A operand (token col, 16-byte chunk 4j + grp); the
         // reads complete before V takes the stage over
-        u32x4 ks[KST ? NJ : 1];
+        // (FP8: rows of D code bytes on the same 2 * VROW-byte pitch; lane reads
+        // the 16 codes of dims 64 m + 16 grp + 0..15 of token col)
+        u32x4 ks[KST ? NK : 1];
         if constexpr (KST) {
+            unsigned char *kst = reinterpret_cast<unsigned char *>(vstage);
 #pragma unroll
-            for (int j = 0; j < NK; ++j) *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW) = kr[j];
+            for (int j = 0; j < NK; ++j)
+                *reinterpret_cast<u32x4 *>(kst + (vrow + j * TPI) * (2 * VROW) + vcol * 16) = kr[j];
             wave_lds_sync();
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                ks[j] = *reinterpret_cast<const u32x4 *>(vstage + col * VROW + (4 * j + grp) * 8);
+            for (int j = 0; j < NK; ++j)
+                ks[j] = *reinterpret_cast<const u32x4 *>(kst + col * (2 * VROW) + (FP8 ? 64 * j + 16 * grp : (4 * j + grp) * 16));
             wave_lds_sync();
         }
         // stage V as bf16 (FP8 codes converted exactly; token rows past the end
@@ -473,7 +479,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         for (int j = 0; j < NJ; ++j) {
             u32x4 ka;
             if constexpr (FP8)
-                ka = e4m3x8_to_bf16x8(kr[j >> 1][2 * (j & 1)], kr[j >> 1][2 * (j & 1) + 1]);
+                ka = e4m3x8_to_bf16x8(ks[j >> 1][2 * (j & 1)], ks[j >> 1][2 * (j & 1) + 1]);
             else if constexpr (KST)
                 ka = ks[j];
             else
@@ -609,13 +615,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
     }
 
     // ---- per-wave totals -------------------------------------------------
-    // (the fused merge needs full barriers; otherwise LDS-only barriers keep
-    // the next item's loads in flight)
+    // (the waves exchange partials through LDS only: LDS-only barriers keep
+    // the next item's prefetched loads in flight; a full __syncthreads would
+    // wait for them on every item)
     const bool fused = prm.counters != nullptr;
-    auto wg_sync = [&]() {
-        if (fused) __syncthreads();
-        else lds_barrier();
-    };
+    auto wg_sync = [&]() { lds_barrier(); };
     l_run = sum_xor32(sum_xor16(l_run));
     wg_sync();  // every wave is done with its staging tile before the buffer is reused
     float *red = lds;                      // [NW][G][D]
@@ -700,7 +704,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             flag[0] = (old == nparts - 1);
         }
-        __syncthreads();
+        lds_barrier();  // the verdict travels through LDS
         if (flag[0]) {
             // The merge runs over (column, slot) pairs: a column is 4
             // consecutive dims of one head; a column's SL slots take the
@@ -754,7 +758,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
 #pragma unroll
                 for (int k = 0; k < 4; ++k) f6[2 + k] = acc[k];
             }
-            __syncthreads();
+            lds_barrier();
             for (int c = tid; c < COLS; c += T) {
                 const int h = c / (D / 4), d0 = 4 * (c % (D / 4));
                 float M = -INFINITY;
