@@ -247,13 +247,6 @@ __device__ __forceinline__ void stage_item_ids(const DecodeItem &it, const TokId
     wave_lds_sync();
 }
 
-// Workgroup barrier for LDS traffic only: unlike __syncthreads it does not
-// wait for the wave's outstanding global loads, so prefetched tiles stay in
-// flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Processes item `it` with the NW waves of the calling workgroup; `lds` is
 // the workgroup's scratch (DecodeShape floats).  `qb` (the item's query rows)
 // and the ring `kbuf`/`vbuf` (its first DEPTH tiles, tile j in slot j) are

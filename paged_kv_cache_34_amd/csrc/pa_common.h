@@ -93,6 +93,13 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier for LDS traffic only: unlike __syncthreads it does not
+// wait for the wave's outstanding global loads or stores, so prefetched tiles and
+// written results stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4 load_u32x4(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -99,10 +99,12 @@ struct __attribute__((aligned(16))) PfLds {
 // tile's whole causal range and every row is written as bf16.  split >= 0:
 // chunk `split` of size prm.chunk; rows whose keys all lie in the first chunk
 // are written as bf16 (by chunk 0), the others leave a partial record for
-// every chunk holding at least one of their keys.
-template <int D, int G>
+// every chunk holding at least one of their keys.  `after_loop` runs in every
+// thread once the last tile is done, before the results are written.
+template <int D, int G, typename AfterLoop>
 __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds, int seq, int kvh,
-                                              int qtile, int key_begin, int key_end, int split) {
+                                              int qtile, int key_begin, int key_end, int split,
+                                              AfterLoop &&after_loop) {
     constexpr int R = kPfSlots / G;        // query rows per workgroup
     constexpr int KROW = D + 8;
     constexpr int VROW = D + 32;
@@ -331,6 +333,7 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
     if constexpr (DEPTH >= 2) if (t0 + 1 < te) step(t0 + 1, std::integral_constant<int, 1>{});
     if constexpr (DEPTH >= 3) if (t0 + 2 < te) step(t0 + 2, std::integral_constant<int, 2>{});
 
+    after_loop();
     const float l_tot = sum_xor32_pf(l_run);
     if (!q_ok) return;
     if (split >= 0 && limit < key_begin) return;  // no key of this row in the chunk
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PfParams p
     if (r0 >= n) return;
     const int c = prm.seq_lens[seq] - n;
     const int kv_end = c + r0 + min(R, n - r0);  // keys [0, kv_end) are visible to some row
-    prefill_range<D, G>(prm, lds, seq, kvh, qtile, 0, kv_end, -1);
+    prefill_range<D, G>(prm, lds, seq, kvh, qtile, 0, kv_end, -1, [] {});
 }
 
 // Split-KV, persistent.  Every workgroup builds the same chunk list in LDS:
@@ -542,15 +545,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
     const int total = F + NR * hkv;
 
     // 3. take chunks: the first is blockIdx.x, the later ones come from the
-    // device counter (offset by the grid)
-    for (bool first = true;; first = false) {
-        int it = blockIdx.x;
-        if (!first) {
-            if (tid == 0) bcast[0] = (int)gridDim.x + atomicAdd(prm.counters, 1);
-            __syncthreads();
-            it = __builtin_amdgcn_readfirstlane(bcast[0]);
-        }
-        if (it >= total) break;
+    // device counter (offset by the grid).  The claim of the next chunk is
+    // issued once the current one's tiles are done, before its results are
+    // written, and travels through LDS, so neither its round trip nor the
+    // results' stores hold up the next chunk's start.
+    int it = blockIdx.x;
+    while (it < total) {
         int p, kvh, split;
         if (it < F) {
             int lo = 0, hi = NP;  // the last pair with fpref[p] <= it
@@ -574,8 +574,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_split_kernel(PfPa
         split = __builtin_amdgcn_readfirstlane(split);
         const int kv_end = __builtin_amdgcn_readfirstlane(pr_kv[p]);
         const int kb = split * C;
+        int claim = 0;
         prefill_range<D, G>(prm, lds, __builtin_amdgcn_readfirstlane(pr_seq[p]), kvh,
-                            __builtin_amdgcn_readfirstlane(pr_qt[p]), kb, min(kb + C, kv_end), split);
+                            __builtin_amdgcn_readfirstlane(pr_qt[p]), kb, min(kb + C, kv_end), split, [&] {
+                                if (tid == 0) claim = (int)gridDim.x + atomicAdd(prm.counters, 1);
+                            });
+        if (tid == 0) bcast[0] = claim;
+        lds_barrier();
+        it = __builtin_amdgcn_readfirstlane(bcast[0]);
     }
     if (tid == 0) {
         const int done = __hip_atomic_fetch_add(prm.counters + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);

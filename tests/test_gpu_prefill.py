@@ -134,6 +134,23 @@ def test_split_long_context_and_counters(orc):
         assert int(ws.buffer[:8].view(torch().int32).abs().sum().item()) == 0
 
 
+@pytest.mark.parametrize("hkv,G", [(16, 2), (24, 1), (4, 8)])
+def test_split_kv_head_counts(orc, hkv, G):
+    """The split form with 16, 24 and 4 kv heads (chunk items per kv head),
+    contexts of a few thousand tokens, 256-token chunks and the automatic
+    chunk; the counters are zero again after every call."""
+    case = workloads.prefill_case(f"plist{hkv}", 706 + hkv, [150, 40, 1, 260], [3000, 4500, 100, 700],
+                                  hkv * G, hkv, 128)
+    ref = orc.prefill_case(case)
+    dev = Dev(case)
+    for chunk in (0, 256):
+        ws = workspace_for(dev, chunk)
+        announce(f"split Hkv={hkv} G={G}, chunk {chunk} (auto={ws.kv_chunk})")
+        got = run_prefill(dev, "split-auto" if chunk == 0 else f"split-{chunk}", ws)
+        assert_out_close(bf16_host_f64(got), ref, f"split Hkv={hkv} chunk {chunk}")
+        assert int(ws.buffer[:8].view(torch().int32).abs().sum().item()) == 0
+
+
 def test_split_falls_back_to_single_pass_without_workspace(orc):
     case = workloads.prefill_case("pfall", 705, [20, 9], [30, 0], 8, 2, 64)
     dev = Dev(case)
