@@ -1314,10 +1314,16 @@ constexpr int decode_depth(int, bool fp8) { return fp8 ? PA_DECODE_DEPTH_FP8 : P
 #ifndef PA_DECODE_PERSIST_PER_CU
 #define PA_DECODE_PERSIST_PER_CU 0   // 0 = as many workgroups per CU as fit
 #endif
-// FP8 caches: at most two persistent workgroups per CU even where three fit
-// (measured on MI355X: a third gains 0.3 us on a 72k-token Llama-3-8B-shaped
-// batch and loses 8 us on a 432k-token ragged G=8 batch)
+// FP8 caches: at most two persistent workgroups per CU where the grid has
+// many items, three where it has at most kFp8FewItemsPerCu per CU.  An FP8
+// tile is half the bytes of a bf16 one, so a few long items leave too little
+// in flight with two; with many items a third only adds cache pressure
+// (measured on MI355X: three take a 72k-token Llama-3-8B-shaped batch of
+// 2,048 items from 36.2-36.6 to 33.4-33.9 us, and a 432k-token ragged G=8
+// batch from 193.5 to 199.8 us; a 400k-token D=256 batch is unchanged).
 constexpr int kFp8PersistPerCu = 2;
+constexpr int kFp8FewItemsPersistPerCu = 3;
+constexpr int kFp8FewItemsPerCu = 8;
 
 
 template <int D, int G, bool FP8, bool XP, bool TOK>
@@ -1351,8 +1357,12 @@ hipError_t launch_decode_dg(const DecodeArgs &a) {
         int per_cu = PA_DECODE_PERSIST_PER_CU > 0
                          ? PA_DECODE_PERSIST_PER_CU
                          : resident_per_cu<paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP, TOK>>(block.x);
-        if (FP8 && per_cu > kFp8PersistPerCu) per_cu = kFp8PersistPerCu;
         const long upper = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
+        if (FP8) {
+            const int most = upper <= (long)kFp8FewItemsPerCu * device_cu_count() ? kFp8FewItemsPersistPerCu
+                                                                                   : kFp8PersistPerCu;
+            if (per_cu > most) per_cu = most;
+        }
         const long cap = (long)device_cu_count() * per_cu;
         dim3 grid((unsigned)(upper < cap ? upper : cap));
         hipLaunchKernelGGL((paged_decode_compact_kernel<D, G, kDecodeWaves, DEPTH, FP8, XP, TOK>), grid, block, 0,
