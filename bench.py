@@ -679,7 +679,9 @@ def secondary_lines(args, pa):
             out[wl]["fused_frac_of_peak"] = r["fused_merge"]["frac_of_peak"]
         torch.cuda.empty_cache()
     sub = argparse.Namespace(**vars(args))
-    sub.workload, sub.steps, sub.warmup, sub.prefill_form = "ragged_prefill", args.secondary_steps, 5, "split"
+    # (the same 20 warmup steps as a ragged_prefill run of its own: the large
+    # ragged decode before it leaves the caches full of its pool)
+    sub.workload, sub.steps, sub.warmup, sub.prefill_form = "ragged_prefill", args.secondary_steps, 20, "split"
     r, _ = run_prefill(sub, pa)
     out["ragged_prefill"] = {"ms_per_step": r["ms_per_step"], "tflops": r["value"],
                              "frac_of_bf16_peak": r["roofline"]["frac"], "kv_chunk": r["config"]["kv_chunk"],
