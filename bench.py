@@ -437,7 +437,8 @@ def gather_ceiling(pa, cases, devs):
     """Paged-gather ceiling from the library's gather probe: the decode's own
     K/V tiles of the rotated pool copies, read through their block tables,
     best over grids of 1..32 workgroups per CU; per-(kv head, block) tiles in
-    the decode's order, and whole blocks (all kv heads of a block together)."""
+    the decode's order, whole blocks (all kv heads of a block together), and
+    the tiles read through load-to-LDS instructions."""
     import numpy as np
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -450,7 +451,7 @@ def gather_ceiling(pa, cases, devs):
     prefd = torch.from_numpy(pref).cuda()
     nbytes = int(pref[-1]) * c0.num_kv_heads * 2 * 16 * c0.head_dim * 2
     out = {}
-    for whole in (False, True):
+    for whole in (0, 1, 2):
         best = None
         for m in (1, 2, 4, 8, 16, 32):
             partial = torch.empty(m * cus, dtype=torch.int32, device="cuda")
@@ -470,17 +471,19 @@ def gather_ceiling(pa, cases, devs):
             ms = e0.elapsed_time(e1) / reps
             if best is None or ms < best[0]:
                 best = (ms, m * cus)
-        key = "gather_blocks" if whole else "gather_tiles"
+        key = ("gather_tiles", "gather_blocks", "gather_tiles_to_lds")[whole]
         out[key + "_gbps"] = nbytes / (best[0] * 1e-3) / 1e9
         out[key + "_ms"] = best[0]
         out[key + "_workgroups"] = best[1]
     out["gather_bytes"] = nbytes
     out["gather_probe"] = ("paged_attn_gather_probe over the decode's rotated pool copies: tiles = the K and V "
                            "tile of one (sequence, kv head, block) per wave in the decode's order; blocks = "
-                           "consecutive waves read one block's H_kv tiles of K then V; best of 1..32 "
-                           "workgroups per CU")
+                           "consecutive waves read one block's H_kv tiles of K then V; tiles_to_lds = the "
+                           "tiles through load-to-LDS instructions into a two-piece LDS ring per wave; best "
+                           "of 1..32 workgroups per CU")
     log(f"gather ceiling: tiles {out['gather_tiles_gbps']:.0f} GB/s ({out['gather_tiles_ms'] * 1e3:.1f} us), "
-        f"whole blocks {out['gather_blocks_gbps']:.0f} GB/s ({out['gather_blocks_ms'] * 1e3:.1f} us)")
+        f"whole blocks {out['gather_blocks_gbps']:.0f} GB/s ({out['gather_blocks_ms'] * 1e3:.1f} us), "
+        f"tiles to LDS {out['gather_tiles_to_lds_gbps']:.0f} GB/s ({out['gather_tiles_to_lds_ms'] * 1e3:.1f} us)")
     return out
 
 

@@ -403,8 +403,11 @@ int paged_attn_read_probe(const void *buf, long long bytes, uint32_t *partial, i
  *                   decode's own walk over scattered tiles;
  *   whole_blocks 1: consecutive tile pairs of [K block | V block] of one
  *                   (sequence, block) -- each block's contiguous
- *                   H_kv * 16 * head_dim K and V rows read together.
- * Both modes read the same bytes.  The grid's waves split the pieces into
+ *                   H_kv * 16 * head_dim K and V rows read together;
+ *   whole_blocks 2: the pieces of mode 0 read with load-to-LDS instructions
+ *                   into a per-wave ring of two pieces in LDS and folded
+ *                   from there -- the gather a direct-to-LDS tile ring sees.
+ * All modes read the same bytes.  The grid's waves split the pieces into
  * equal consecutive runs.  partial[w] receives the XOR of the 32-bit words
  * workgroup w read; the XOR over all entries equals the XOR of every 32-bit
  * word of the K and V tiles of the used blocks (a block used twice cancels).
@@ -415,8 +418,9 @@ int paged_attn_read_probe(const void *buf, long long bytes, uint32_t *partial, i
  *                     block_prefix[s + 1] - block_prefix[s] = ceil(L_s / 16).
  *   partial           uint32 [num_workgroups], device, written only.
  * Limits: num_seqs <= 1024, head_dim in {64, 128, 256}, block_size 16.
- * Errors: PA_ERR_NULL_POINTER, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED,
- * PA_ERR_ALIGNMENT, PA_ERR_LAUNCH.  Enqueued on `stream`.
+ * Errors: PA_ERR_NULL_POINTER, PA_ERR_BAD_SHAPE (including whole_blocks
+ * outside 0..2), PA_ERR_UNSUPPORTED, PA_ERR_ALIGNMENT, PA_ERR_LAUNCH.
+ * Enqueued on `stream`.
  */
 int paged_attn_gather_probe(const void *k_cache, const void *v_cache, const int32_t *block_tables,
                             const int32_t *block_prefix, int num_seqs, int num_kv_heads, int head_dim,

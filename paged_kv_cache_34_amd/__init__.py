@@ -550,12 +550,14 @@ def paged_attn_read_probe(buf, partial, stream=None) -> None:
            library().paged_attn_read_probe(_ptr(buf), nbytes, _ptr(partial), partial.numel(), _stream(stream)))
 
 
-def paged_attn_gather_probe(k_cache, v_cache, block_tables, block_prefix, whole_blocks: bool, partial,
+def paged_attn_gather_probe(k_cache, v_cache, block_tables, block_prefix, whole_blocks, partial,
                             stream=None) -> None:
     """Paged-gather read probe over the K/V tiles a decode of the batch reads
     (block_prefix int32 [num_seqs + 1]: prefix sums of ceil(L / 16)); one
     workgroup per element of the int32 tensor `partial`, which receives each
-    workgroup's XOR of the 32-bit words it read."""
+    workgroup's XOR of the 32-bit words it read.  whole_blocks: 0 (or False)
+    per-(kv head, block) tiles, 1 (or True) whole blocks, 2 the tiles of 0
+    through load-to-LDS instructions."""
     import torch
     _want(k_cache, torch.bfloat16, "k_cache")
     _want(v_cache, torch.bfloat16, "v_cache")
@@ -570,7 +572,7 @@ def paged_attn_gather_probe(k_cache, v_cache, block_tables, block_prefix, whole_
     _check("paged_attn_gather_probe",
            library().paged_attn_gather_probe(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                              _ptr(block_prefix), num_seqs, hkv, d, bs, block_tables.shape[1],
-                                             int(bool(whole_blocks)), _ptr(partial), partial.numel(),
+                                             int(whole_blocks), _ptr(partial), partial.numel(),
                                              _stream(stream)))
 
 

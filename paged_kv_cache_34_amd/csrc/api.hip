@@ -271,7 +271,7 @@ int paged_attn_gather_probe(const void *k_cache, const void *v_cache, const int3
                             int num_workgroups, void *stream) {
     if (!k_cache || !v_cache || !block_tables || !block_prefix || !partial) return PA_ERR_NULL_POINTER;
     if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_workgroups <= 0 ||
-        (whole_blocks != 0 && whole_blocks != 1))
+        whole_blocks < 0 || whole_blocks > 2)
         return PA_ERR_BAD_SHAPE;
     if (!head_dim_ok(head_dim) || block_size != kBlockSize || num_seqs > 1024) return PA_ERR_UNSUPPORTED;
     if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGNMENT;

@@ -68,12 +68,26 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const u32
 //                     (sequence, logical block), pieces ordered (sequence,
 //                     block, i): consecutive waves read each block's
 //                     contiguous H_kv * 16 * D K and V rows.
-// Both modes read the same bytes.  Wave v of the grid takes pieces
+//   whole_blocks = 2: the pieces of mode 0, read with load-to-LDS
+//                     instructions (`buffer_load_dwordx4 ... lds`) into a
+//                     per-wave ring of two pieces in LDS, each waited for
+//                     with a counted vmcnt and then folded from LDS: the
+//                     gather a direct-to-LDS tile ring would see.
+// All modes read the same bytes.  Wave v of the grid takes pieces
 // [v * n, (v + 1) * n), n = ceil(pieces / waves); absent pieces have empty
 // buffer descriptors, whose loads return zeros without touching memory.
 constexpr int kGatherMaxSeqs = 1024;
 
-template <int D>
+// The LDS destination of a load-to-LDS instruction, as a wave-uniform
+// address.  The probe orders these writes itself (a counted vmcnt wait before
+// a stage is read, the wave's own loads only), so the compiler is not left to
+// pair them with the reads of the other stage.
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_dest(u32x4 *p) {
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4 *)p;
+    return (__attribute__((address_space(3))) void *)(uintptr_t)__builtin_amdgcn_readfirstlane((int)a);
+}
+
+template <int D, bool TO_LDS>
 __global__ __launch_bounds__(kProbeThreads) void paged_gather_probe_kernel(
     const char *__restrict__ k_cache, const char *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ block_prefix, int num_seqs, int num_kv_heads, int max_blocks_per_seq,
@@ -82,6 +96,7 @@ __global__ __launch_bounds__(kProbeThreads) void paged_gather_probe_kernel(
     constexpr int W = TILE / (64 * 16);      // 16-byte loads per lane per tile
     __shared__ int pref[kGatherMaxSeqs + 1];
     __shared__ uint32_t wave_acc[kProbeThreads / 64];
+    __shared__ __attribute__((aligned(16))) u32x4 lring[TO_LDS ? (kProbeThreads / 64) * 2 * 2 * W * 64 : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int i = tid; i <= num_seqs; i += kProbeThreads) pref[i] = block_prefix[i];
@@ -129,6 +144,51 @@ __global__ __launch_bounds__(kProbeThreads) void paged_gather_probe_kernel(
             }
         }
         const uint64_t u0 = reinterpret_cast<uint64_t>(a0), u1 = reinterpret_cast<uint64_t>(a1);
+        if constexpr (TO_LDS) {
+            // two stages of one piece (K tile then V tile, 64 lanes x 16
+            // bytes per load) in this wave's LDS region
+            auto stage = [&](int st) { return &lring[((wave * 2 + st) * 2 * W) * 64]; };
+            auto issue_lds = [&](int i, int st) {
+                const int j = i < n ? i : 0;
+                const int bytes = i < n ? TILE : 0;
+                const uint64_t b0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(u0 >> 32), j) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u0, j);
+                const uint64_t b1 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(u1 >> 32), j) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u1, j);
+                const auto r0 = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(b0), 0, bytes, kProbeBufferFlags);
+                const auto r1 = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(b1), 0, bytes, kProbeBufferFlags);
+                u32x4 *dst = stage(st);
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, lds_dest(dst + w * 64), 16, 16 * lane + 1024 * w, 0, 0, 2);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, lds_dest(dst + (W + w) * 64), 16, 16 * lane + 1024 * w, 0,
+                                                             0, 2);
+                }
+            };
+            // (vmcnt in the s_waitcnt encoding: low 4 bits, high 2 bits at
+            // 14..15; expcnt 7 and lgkmcnt 15 mean no wait on those counters)
+            constexpr int NL = 2 * W;  // load instructions of one piece
+            auto fold_lds = [&](int st) {
+                __builtin_amdgcn_s_waitcnt((NL & 15) | ((NL >> 4) << 14) | (7 << 4) | (15 << 8));
+                const u32x4 *src = stage(st);
+#pragma unroll
+                for (int w = 0; w < 2 * W; ++w) {
+                    const u32x4 r = src[w * 64 + lane];
+                    acc ^= (r[0] ^ r[1]) ^ (r[2] ^ r[3]);
+                }
+                // the stage's reads complete before the next loads into it are issued
+                __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+            };
+            issue_lds(0, 0);
+            for (int i = 0; i < n; i += 2) {
+                issue_lds(i + 1, 1);
+                fold_lds(0);  // piece i (the one issued before piece i + 1)
+                issue_lds(i + 2, 0);
+                fold_lds(1);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // the last issue (zeros) lands before the next chunk
+            continue;
+        }
         u32x4 ring[2][2 * W];
         auto issue = [&](int i, u32x4 (&r)[2 * W]) {
             const int j = i < n ? i : 0;
@@ -176,8 +236,13 @@ hipError_t launch_gather_probe(const void *k_cache, const void *v_cache, const i
                                const int32_t *block_prefix, int num_seqs, int num_kv_heads, int head_dim,
                                int max_blocks_per_seq, int whole_blocks, uint32_t *partial, int num_workgroups,
                                hipStream_t stream) {
-    auto kern = head_dim == 64 ? paged_gather_probe_kernel<64>
-              : head_dim == 128 ? paged_gather_probe_kernel<128> : paged_gather_probe_kernel<256>;
+    auto kern = whole_blocks == 2
+                    ? (head_dim == 64    ? paged_gather_probe_kernel<64, true>
+                       : head_dim == 128 ? paged_gather_probe_kernel<128, true>
+                                         : paged_gather_probe_kernel<256, true>)
+                    : (head_dim == 64    ? paged_gather_probe_kernel<64, false>
+                       : head_dim == 128 ? paged_gather_probe_kernel<128, false>
+                                         : paged_gather_probe_kernel<256, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)num_workgroups), dim3(kProbeThreads), 0, stream,
                        static_cast<const char *>(k_cache), static_cast<const char *>(v_cache), block_tables,
                        block_prefix, num_seqs, num_kv_heads, max_blocks_per_seq, whole_blocks, partial);

@@ -491,7 +491,8 @@ def test_noalloc_validation(lib, over, status):
 
 @pytest.mark.parametrize("over,status", [
     (dict(k=None), pa.PA_ERR_NULL_POINTER), (dict(pref=None), pa.PA_ERR_NULL_POINTER),
-    (dict(S=0), pa.PA_ERR_BAD_SHAPE), (dict(nwg=0), pa.PA_ERR_BAD_SHAPE), (dict(whole=2), pa.PA_ERR_BAD_SHAPE),
+    (dict(S=0), pa.PA_ERR_BAD_SHAPE), (dict(nwg=0), pa.PA_ERR_BAD_SHAPE), (dict(whole=3), pa.PA_ERR_BAD_SHAPE),
+    (dict(whole=-1), pa.PA_ERR_BAD_SHAPE),
     (dict(D=96), pa.PA_ERR_UNSUPPORTED), (dict(bs=32), pa.PA_ERR_UNSUPPORTED), (dict(S=1025), pa.PA_ERR_UNSUPPORTED),
     (dict(k=8), pa.PA_ERR_ALIGNMENT),
 ])

@@ -62,7 +62,7 @@ def used_tiles_xor(case) -> int:
     ([300, 1000], 4, 256, 512),
     ([5] * 40, 3, 64, 7),            # odd kv head count: a piece straddles K and V
 ])
-@pytest.mark.parametrize("whole", [False, True])
+@pytest.mark.parametrize("whole", [0, 1, 2])
 def test_gather_probe_xor(lens, hkv, D, nwg, whole):
     import workloads
     t = torch()
