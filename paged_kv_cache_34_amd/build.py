@@ -4,7 +4,12 @@ Usage: python -m paged_kv_cache_34_amd.build   (or build() from Python)
 
 Each translation unit under csrc/ is compiled in parallel into _build/, then
 linked into paged_kv_cache_34_amd/libpaged_attn.so next to this file.  All
-device code is built with packed-fp32 instructions disabled.
+device code is built with packed-fp32 instructions disabled.  Extra hipcc
+flags may be given in the environment variable PA_HIPCC_FLAGS (whitespace
+separated), e.g. the compile-time tuning macros of csrc/decode_kernels.h
+(PA_DECODE_DEPTH, PA_DECODE_DEPTH_FP8, PA_DECODE_PERSIST_PER_CU,
+PA_FP8_FEW_ITEMS_PERSIST_PER_CU) to reproduce the variants those macros
+document.
 """
 from __future__ import annotations
 
@@ -40,7 +45,8 @@ def _flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
+            "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"] + \
+        os.environ.get("PA_HIPCC_FLAGS", "").split()
 
 
 def _compile(src: str) -> str:

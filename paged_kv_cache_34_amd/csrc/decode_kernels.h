@@ -1321,8 +1321,11 @@ constexpr int decode_depth(int, bool fp8) { return fp8 ? PA_DECODE_DEPTH_FP8 : P
 // (measured on MI355X: three take a 72k-token Llama-3-8B-shaped batch of
 // 2,048 items from 36.2-36.6 to 33.4-33.9 us, and a 432k-token ragged G=8
 // batch from 193.5 to 199.8 us; a 400k-token D=256 batch is unchanged).
+#ifndef PA_FP8_FEW_ITEMS_PERSIST_PER_CU
+#define PA_FP8_FEW_ITEMS_PERSIST_PER_CU 3  // (2 reproduces the cap before the rule)
+#endif
 constexpr int kFp8PersistPerCu = 2;
-constexpr int kFp8FewItemsPersistPerCu = 3;
+constexpr int kFp8FewItemsPersistPerCu = PA_FP8_FEW_ITEMS_PERSIST_PER_CU;
 constexpr int kFp8FewItemsPerCu = 8;
 
 
