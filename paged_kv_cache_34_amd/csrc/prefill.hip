@@ -234,6 +234,19 @@ __device__ __forceinline__ void prefill_range(const PfParams &prm, PfLds<D> &lds
                                                                __builtin_bit_cast(bf16x8, qf[kk]), s[a], 0, 0, 0);
             }
         }
+        // keep SAHEAD K operand reads in flight ahead of the MFMAs (the
+        // compiler's own order issues them one MFMA ahead); D = 256 has no
+        // registers to spare for them
+        if constexpr (D <= 128) {
+            constexpr int NSM = NK * NSA, SAHEAD = NSM < 4 ? NSM : 4;
+            __builtin_amdgcn_sched_group_barrier(0x100, SAHEAD, 0);  // DS reads
+#pragma unroll
+            for (int z = 0; z < NSM - SAHEAD; ++z) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, SAHEAD, 0);
+        }
         // lane holds tokens 32a + (i/4)*8 + 4*grp + i%4 of this tile for query
         // slot `col`; only tiles reaching past the first row's causal limit
         // (or the end of the visible keys) need the mask.  With scale > 0 the
