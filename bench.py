@@ -444,18 +444,23 @@ def gather_ceiling(pa, cases, devs):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     c0 = cases[0]
-    if c0.num_seqs > 1024 or c0.head_dim not in (64, 128, 256):
+    # an E4M3 cache (one byte per element) is read as bf16 tiles of half the
+    # head dim: the same bytes, block by block (its scales are not read)
+    fp8 = devs[0]["k"].dtype == torch.uint8
+    probe_d = c0.head_dim // 2 if fp8 else c0.head_dim
+    if c0.num_seqs > 1024 or probe_d not in (64, 128, 256):
         return {}
+    view = (lambda t: t.view(torch.bfloat16)) if fp8 else (lambda t: t)
     pref = np.zeros(c0.num_seqs + 1, np.int32)
     pref[1:] = np.cumsum((c0.seq_lens.astype(np.int64) + 15) // 16)
     prefd = torch.from_numpy(pref).cuda()
-    nbytes = int(pref[-1]) * c0.num_kv_heads * 2 * 16 * c0.head_dim * 2
+    nbytes = int(pref[-1]) * c0.num_kv_heads * 2 * 16 * probe_d * 2
     out = {}
     for whole in (0, 1, 2):
         best = None
         for m in (1, 2, 4, 8, 16, 32):
             partial = torch.empty(m * cus, dtype=torch.int32, device="cuda")
-            call = lambda i: pa.paged_attn_gather_probe(devs[i % len(devs)]["k"], devs[i % len(devs)]["v"],
+            call = lambda i: pa.paged_attn_gather_probe(view(devs[i % len(devs)]["k"]), view(devs[i % len(devs)]["v"]),
                                                         devs[i % len(devs)]["bt"], prefd, whole, partial,
                                                         stream=stream)
             for i in range(3):
@@ -480,7 +485,8 @@ def gather_ceiling(pa, cases, devs):
                            "tile of one (sequence, kv head, block) per wave in the decode's order; blocks = "
                            "consecutive waves read one block's H_kv tiles of K then V; tiles_to_lds = the "
                            "tiles through load-to-LDS instructions into a two-piece LDS ring per wave; best "
-                           "of 1..32 workgroups per CU")
+                           "of 1..32 workgroups per CU" + ("; E4M3 cache: its code tiles read as bf16 tiles of "
+                           "half the head dim (gather_bytes = the codes, without the scales)" if fp8 else ""))
     log(f"gather ceiling: tiles {out['gather_tiles_gbps']:.0f} GB/s ({out['gather_tiles_ms'] * 1e3:.1f} us), "
         f"whole blocks {out['gather_blocks_gbps']:.0f} GB/s ({out['gather_blocks_ms'] * 1e3:.1f} us), "
         f"tiles to LDS {out['gather_tiles_to_lds_gbps']:.0f} GB/s ({out['gather_tiles_to_lds_ms'] * 1e3:.1f} us)")
