@@ -458,9 +458,17 @@ __device__ __forceinline__ void decode_item(const DecodeParams &prm, const Decod
         for (int j = 0; j < (XP ? 0 : NV); ++j) {
             const bool dead = tail && tb + vrow + j * TPI >= t_end;
             if constexpr (FP8) {
+                // every lane converts (a per-lane choice would put each
+                // conversion under its own exec mask); only the sequence's
+                // last tile, a wave-uniform case, masks its dead rows after
                 const u32x4 w = vr[j];
-                const u32x4 lo = dead ? u32x4{0u, 0u, 0u, 0u} : e4m3x8_to_bf16x8(w[0], w[1]);
-                const u32x4 hi = dead ? u32x4{0u, 0u, 0u, 0u} : e4m3x8_to_bf16x8(w[2], w[3]);
+                u32x4 lo = e4m3x8_to_bf16x8(w[0], w[1]);
+                u32x4 hi = e4m3x8_to_bf16x8(w[2], w[3]);
+                if (tail) {
+                    const uint32_t keep = dead ? 0u : 0xffffffffu;
+                    lo &= keep;
+                    hi &= keep;
+                }
                 *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW) = lo;
                 *reinterpret_cast<u32x4 *>(vst_wr + j * TPI * VROW + 8) = hi;
             } else {
