@@ -332,7 +332,7 @@ int paged_attn_prefill_ragged_split(const void *q, const void *k_cache, const vo
 
 /* ---- host-only helpers (no device work) ---------------------------------- */
 
-/* Key chunk the split-KV prefill uses when kv_chunk == 0: about three chunks
+/* Key chunk the split-KV prefill uses when kv_chunk == 0: about 2.6 chunks
  * per CU of the current device if every (sequence, query tile) pair had the
  * longest context, a multiple of 256 in [512, 8192]; 0 when the single pass
  * is used instead (too many pairs or query heads, or one chunk covers the

@@ -480,13 +480,13 @@ int paged_attn_prefill_chunk_size(int num_seqs, int total_q, int num_q_heads, in
     const long long pairs = ceil_div(total_q, rows) + num_seqs;
     if (num_seqs > pa::kPfMaxSeqs || pairs > pa::kPfMaxPairs || num_q_heads > pa::kPfMaxHeads) return 0;
     const long long lmax = (long long)max_blocks_per_seq * block_size;
-    // about three chunks per CU if every pair had the longest context
-    // (measured on MI355X over 512..8192-token chunks on a ragged batch of
-    // 16 sequences: fewer, longer chunks win until the last ones unbalance
-    // the grid -- each chunk costs a start-up of dependent loads and its
-    // rows' partial records)
-    const long long target = 3LL * pa::device_cu_count();
-    long long chunk = ceil_div(pairs * num_kv_heads * lmax, target);
+    // about 2.6 chunks per CU (13 per 5 CUs) if every pair had the longest
+    // context (measured on MI355X over 512..8192-token chunks on a ragged
+    // batch of 16 sequences: fewer, longer chunks win until the last ones
+    // unbalance the grid -- each chunk costs a start-up of dependent loads
+    // and its rows' partial records; 2.6 per CU beat 3 by 3%)
+    const long long target = 13LL * pa::device_cu_count();
+    long long chunk = ceil_div(pairs * num_kv_heads * lmax * 5, target);
     chunk = ceil_div(chunk, kChunkQuantum) * kChunkQuantum;
     if (chunk < kMinChunk) chunk = kMinChunk;
     if (chunk > pa::kPfMaxChunk) chunk = pa::kPfMaxChunk;

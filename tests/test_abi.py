@@ -241,12 +241,14 @@ def test_prefill_workspace_size_formula(lib):
 
 def test_prefill_chunk_size_heuristic(lib):
     # Without a GPU the device has 256 CUs in this formula: chunk =
-    # ceil((ceil(total_q / (256 / G)) + S) * H_kv * L_max / (3 * 256)), rounded up
-    # to 256, clamped to [512, 8192]; 0 when it covers L_max or the pairs overflow.
-    # ragged prefill shape: 16 sequences, 1815 rows, G = 4, L_max = 525 * 16
-    assert pa.paged_attn_prefill_chunk_size(16, 1815, 32, 8, 525, 16) == 4096
-    # one sequence, 64 new rows after a 100k context: many chunks for 8 workgroups
-    assert pa.paged_attn_prefill_chunk_size(1, 64, 32, 8, 6250, 16) == 2304
+    # ceil((ceil(total_q / (256 / G)) + S) * H_kv * L_max * 5 / (13 * 256)), rounded
+    # up to 256, clamped to [512, 8192]; 0 when it covers L_max or the pairs overflow.
+    # ragged prefill shape: 16 sequences, 1815 rows, G = 4, L_max = 525 * 16:
+    # 45 * 8 * 8400 * 5 / 3328 = 4543.3 -> 4608
+    assert pa.paged_attn_prefill_chunk_size(16, 1815, 32, 8, 525, 16) == 4608
+    # one sequence, 64 new rows after a 100k context: 2 * 8 * 100000 * 5 / 3328
+    # = 2403.8 -> 2560, many chunks for 8 workgroups
+    assert pa.paged_attn_prefill_chunk_size(1, 64, 32, 8, 6250, 16) == 2560
     # short contexts: one chunk would cover them, so single pass
     assert pa.paged_attn_prefill_chunk_size(4, 100, 32, 8, 8, 16) == 0
     # more than 1024 (sequence, query tile) pairs: single pass
