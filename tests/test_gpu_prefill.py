@@ -123,7 +123,9 @@ def test_split_long_context_and_counters(orc):
     case = workloads.prefill_case("plong", 704, [200, 3, 64, 129], [6000, 7000, 0, 2500], 32, 8, 128)
     ref = orc.prefill_case(case)
     dev = Dev(case)
-    for chunk in (0, 64, 256, 2048):  # 64: over 64 chunks per row, the merge's multi-pass path
+    # 64: over 64 chunks per row, the merge's multi-pass path; 192 and 4608:
+    # chunks that are not powers of two (the automatic choice is a multiple of 256)
+    for chunk in (0, 64, 192, 256, 2048, 4608):
         ws = workspace_for(dev, chunk)
         announce(f"long contexts, chunk {chunk} (auto={ws.kv_chunk})")
         first = run_prefill(dev, "split-auto" if chunk == 0 else f"split-{chunk}", ws)
